@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Throughput of the blockwise-FP8 ZeRO-1 shard step on one MI355X.
+
+One step = the whole per-step path on one rank's shard: fold of the reduced
+row-major FP32 grads (with the per-slot sums of squares fused in when
+statistics are on) -> statistics finalize -> AdamW + per-block amax + E4M3
+requant -> unfold of the FP8 codes and scales to row-major.  Inputs (row-major
+grads, folded master/m/v, state) are resident in HBM before timing starts.
+
+Default workload: the MoE expert shard -- params [64,2048,7168] x2 and
+[64,7168,2048] FP32, block-wise split over DP = 8, rank 5 (352,321,536 real
+elements), grads N(0,1e-4) x lognormal(0,1) per expert, no clipping.
+
+Prints one JSON line (rank 0).  `value` = real elements of the shard updated
+per second.  `roofline` is for the dominant call (fp8z1_step: the update
+kernel plus its one-workgroup finalize kernel), timed with HIP events on the
+stream the kernels run on; `cpu_baseline` is the numpy oracle on a bounded
+sample of the same shard.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BLOCK = 128 * 128
+
+# Algorithmic bytes per real element (and per slot) of each call, see the design doc.
+BYTES_FOLD_F32 = 8  # read 4, write 4
+BYTES_STATS = 4  # separate statistics kernel (not used when fused into the fold)
+BYTES_UPDATE = 29  # read g, p, m, v (16); write p, m, v (12) + code (1)
+BYTES_UNFOLD_E4M3 = 2  # read code, write code
+SLOT_BYTES_UPDATE = 32 + 4  # slot plan record + scale
+SLOT_BYTES_FOLD = 32 + 8  # slot plan record + fused per-slot sum
+SLOT_BYTES_UNFOLD = 32 + 8  # slot plan record + scale read and write
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _gen_params(w, held, make, dtype):
+    import torch
+    out = []
+    jobs = []
+    for pid, (E, R, C) in enumerate(w.shapes):
+        if pid not in held:
+            out.append(None)
+            continue
+        t = torch.zeros((E, R, C), dtype=dtype, device="cuda")
+        out.append(t)
+        jobs += [(pid, e) for e in held[pid]]
+
+    def one(job):
+        pid, e = job
+        return job, make(pid, e)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        for (pid, e), slab in ex.map(one, jobs):
+            src = torch.from_numpy(slab.view(np.int16) if dtype == torch.bfloat16 else slab)
+            if dtype == torch.bfloat16:
+                src = src.view(torch.bfloat16)
+            out[pid][e].copy_(src)
+    return out
+
+
+def _held(entries):
+    held = {}
+    for p, e in zip(entries["param"], entries["expert"]):
+        if p >= 0:
+            held.setdefault(int(p), set()).add(int(e))
+    return {p: sorted(s) for p, s in held.items()}
+
+
+def _source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "blockwise_fp8_zero_fold_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str, src_hash: str):
+    """HBM bytes per fp8z1_step launch from the committed rocprofv3 counter summary,
+    or None when the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"update_kernel_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except ValueError:
+        return None
+    if rec.get("source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, rank: int, slots: int):
+    """The oracle (numpy, as committed) on a bounded sample of the same shard: fold of
+    grads, one step, unfold of the codes, over the first ``slots`` slots."""
+    from oracle import layout, optim, step, table
+
+    tab = table.build(w.shapes, w.dp, rank, table.PARAM if w.split == "param" else table.BLOCK)
+    sub = dict(tab)
+    sub["entries"] = tab["entries"][:slots]
+    sub["shard_slots"] = slots
+    held = _held(sub["entries"])
+    G = {p: np.zeros(w.shapes[p], np.float32) for p in held}
+    P = {p: np.zeros(w.shapes[p], np.float32) for p in held}
+    for p, es in held.items():
+        for e in es:
+            G[p][e] = synth.grad_slab(w, p, e, 1)
+            P[p][e] = synth.master_slab(w, p, e)
+    master = layout.fold_shard(sub, P)
+    n = slots
+    z = np.zeros((n, 128, 128), np.float32)
+    codes = np.zeros((n, 128, 128), np.uint8)
+    sc = np.zeros(n, np.float32)
+    out = {p: np.zeros(w.shapes[p], np.uint8) for p in held}
+    t0 = time.perf_counter()
+    g = layout.fold_shard(sub, G)
+    st, master, m, v, codes, sc = step.step_sharded(sub, w.hp, optim.init_state(w.hp), g, master, z, z, codes, sc)
+    layout.unfold_shard(sub, codes, out)
+    dt = time.perf_counter() - t0
+    valid = int(np.sum(sub["entries"]["vrows"].astype(np.int64) * sub["entries"]["vcols"]))
+    return valid / dt, valid, dt
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="moe", choices=["moe", "dense", "full", "ragged"])
+    ap.add_argument("--unfused-stats", action="store_true", help="separate statistics kernel instead of fold-fused")
+    ap.add_argument("--cpu-slots", type=int, default=2048, help="oracle sample size (slots) for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU path is a design, not a runnable configuration", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import blockwise_fp8_zero_fold_amd as fz
+    from blockwise_fp8_zero_fold_amd.shard import Shard
+
+    w = synth.get(args.workload)
+    rank = w.ranks[0]
+    split = fz.SPLIT_PARAM if w.split == "param" else fz.SPLIT_BLOCK
+    torch.cuda.set_device(0)
+    t_setup = time.perf_counter()
+    sh = Shard(w.shapes, w.dp, rank, split)
+    info = sh.table.info
+    valid = info["valid_elems"]
+    nslots = info["shard_slots"]
+    held = _held(sh.table.entries())
+    print(f"# setup: {w.name} rank {rank}: {nslots} slots, {valid} real elements", file=sys.stderr, flush=True)
+    if w.master_dtype == "bf16":
+        weights = _gen_params(w, held, lambda p, e: synth.master_slab_bf16(w, p, e), torch.bfloat16)
+        wdt = fz.BF16
+    else:
+        weights = _gen_params(w, held, lambda p, e: synth.master_slab(w, p, e), torch.float32)
+        wdt = fz.F32
+    sh.init(fz.Hparams.make(w.hp), weights, wdt)
+    del weights
+    grads = _gen_params(w, held, lambda p, e: synth.grad_slab(w, p, e, 1), torch.float32)
+    codes = [torch.zeros(s, dtype=torch.uint8, device="cuda") if p in held else None for p, s in enumerate(w.shapes)]
+    scales = [torch.zeros((s[0], -(-s[1] // 128), -(-s[2] // 128)), dtype=torch.float32, device="cuda")
+              if p in held else None for p, s in enumerate(w.shapes)]
+    hp = fz.Hparams.make(w.hp)
+    stats = w.hp.max_grad_norm > 0 or w.hp.loss_scaling
+    fused = stats and not args.unfused_stats
+    torch.cuda.synchronize()
+    print(f"# setup done in {time.perf_counter() - t_setup:.1f}s; warmup {args.warmup}, timed {args.steps}",
+          file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        sh.step(hp, grads, codes, scales, fused_stats=fused)
+    torch.cuda.synchronize()
+
+    ev = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(args.steps)],
+              [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]) for k in ("fold", "step", "unfold")}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev["fold"][0][i].record(stream)
+        pre = sh.fold_grads(hp, grads, fused_stats=fused)
+        ev["fold"][1][i].record(stream)
+        ev["step"][0][i].record(stream)
+        sh.update(hp, presummed=pre)
+        ev["step"][1][i].record(stream)
+        ev["unfold"][0][i].record(stream)
+        sh.unfold(codes, scales)
+        ev["unfold"][1][i].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in zip(*ev[k])])) for k in ev}
+    st = sh.read_state()
+    print(f"# timed {args.steps} steps in {elapsed:.3f}s; per call ms: {ms}; state step {st['step']}",
+          file=sys.stderr, flush=True)
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    upd_bytes = BYTES_UPDATE * valid + SLOT_BYTES_UPDATE * nslots
+    step_bytes = ((BYTES_FOLD_F32 * valid + SLOT_BYTES_FOLD * nslots) + upd_bytes
+                  + (BYTES_STATS * valid if stats and not fused else 0)
+                  + BYTES_UNFOLD_E4M3 * valid + SLOT_BYTES_UNFOLD * nslots)
+    achieved = upd_bytes / (ms["step"] * 1e-3) / 1e9
+    src_hash = _source_hash()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        slots = min(args.cpu_slots, nslots)
+        print(f"# cpu baseline: oracle on {slots} slots", file=sys.stderr, flush=True)
+        rate, n_el, dt = cpu_baseline(w, rank, slots)
+        cpu = {"value": rate, "unit": "elements/s", "cores": 1, "kind": "oracle",
+               "sample": f"fold+step+unfold of the first {slots} slots ({n_el} real elements) of the same shard, "
+                         f"numpy, one thread, {dt:.1f}s"}
+
+    out = {
+        "metric": "optimizer-step elements/s and GB/s (% of HBM peak) per 1-GPU shard",
+        "value": valid / (ms_per_step * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": {"moe": "moe_expert_shard", "dense": "dense_layer_set", "full": "full_step_bf16",
+                         "ragged": "ragged_600_params"}[w.name],
+            "shapes": [list(s) for s in w.shapes], "dp": w.dp, "rank": rank,
+            "split": w.split, "shard_slots": nslots, "valid_elems": valid,
+            "clip": w.hp.max_grad_norm, "loss_scaling": bool(w.hp.loss_scaling),
+            "stats": "fused-in-fold" if fused else ("separate" if stats else "off"),
+        },
+        "gbs_algorithmic": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac_step": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "per_call_ms": ms,
+        "roofline": {
+            "kernel": "fp8z1_step (update_kernel + finalize_kernel)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": _traffic(w.name, src_hash),
+            "bytes_per_launch": upd_bytes,
+        },
+        "cpu_baseline": cpu,
+        "source_hash": src_hash,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,147 @@
+// Fold: row-major [E, R, C] params -> the shard's 128x128-block-contiguous
+// float32 buffer ("面向 Blockwise FP8 量化的 ZeRO 优化器设计", section
+// "参数布局变换"; padding of section "块粒度切分").
+//
+// Inside a block the element order stays row-major: the fold's permute
+// swaps the block-column index with the row-within-block index, so each
+// 128-element row segment of the source moves whole to a contiguous 512-byte
+// destination.  The kernel is therefore a segment gather, not a transpose:
+// one workgroup per slot, 32 lanes per row segment, 16-byte loads and stores
+// when the source rows are 16-byte aligned (C % 4 == 0 for float32), element
+// loads with masks otherwise.  Every source byte is read once, every
+// destination byte written once.
+#include <hip/hip_runtime.h>
+
+#include "device_util.h"
+
+namespace fp8z1 {
+namespace {
+
+constexpr int kFoldThreads = kSumThreads;  // also the statistics order
+constexpr int kPasses = kChunks / kFoldThreads;
+
+template <typename T>
+struct Src;
+template <>
+struct Src<float> {
+  static constexpr int kAlign = 16;
+  __device__ static float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static float load1(const float* p) { return *p; }
+};
+template <>
+struct Src<uint16_t> {  // bfloat16 bits
+  static constexpr int kAlign = 8;
+  __device__ static float widen(uint32_t b) { return __uint_as_float(b << 16); }
+  __device__ static float4 load4(const uint16_t* p) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(widen(u.x & 0xffffu), widen(u.x >> 16), widen(u.y & 0xffffu), widen(u.y >> 16));
+  }
+  __device__ static float load1(const uint16_t* p) { return widen(*p); }
+};
+
+template <typename T, bool SUMSQ>
+__global__ __launch_bounds__(kFoldThreads) void fold_kernel(const SlotPlan* __restrict__ plan,
+                                                            const void* const* __restrict__ srcs,
+                                                            float* __restrict__ dst,
+                                                            double* __restrict__ slot_sumsq) {
+  __shared__ double red[kFoldThreads / 64];
+  const int64_t s = blockIdx.x;
+  const SlotPlan P = plan[s];
+  float4* out = reinterpret_cast<float4*>(dst + s * kBlockElems);
+  const int t = threadIdx.x;
+  double acc = 0.0;
+
+  if (P.param < 0) {
+#pragma unroll
+    for (int k = 0; k < kPasses; ++k) out[t + kFoldThreads * k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+    const T* src = static_cast<const T*>(srcs[P.param]) + P.off;
+    const int64_t ld = P.ld;
+    const int vr = P.vr, vc = P.vc;
+    const bool fast = vr == kB && vc == kB && (ld % 4) == 0 &&
+                      (reinterpret_cast<uintptr_t>(src) % Src<T>::kAlign) == 0;
+    float4 x[kPasses];
+    if (fast) {
+#pragma unroll
+      for (int k = 0; k < kPasses; ++k) {
+        const int c = t + kFoldThreads * k;
+        x[k] = Src<T>::load4(src + (c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow));
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kPasses; ++k) {
+        const int c = t + kFoldThreads * k;
+        const int i = c / kChunksPerRow, j = 4 * (c % kChunksPerRow);
+        const T* row = src + i * ld + j;
+        const bool rv = i < vr;
+        x[k].x = (rv && j + 0 < vc) ? Src<T>::load1(row + 0) : 0.f;
+        x[k].y = (rv && j + 1 < vc) ? Src<T>::load1(row + 1) : 0.f;
+        x[k].z = (rv && j + 2 < vc) ? Src<T>::load1(row + 2) : 0.f;
+        x[k].w = (rv && j + 3 < vc) ? Src<T>::load1(row + 3) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPasses; ++k) {
+      out[t + kFoldThreads * k] = x[k];
+      if (SUMSQ) {
+        // padding positions hold +0 and add nothing
+        acc += sq64(x[k].x);
+        acc += sq64(x[k].y);
+        acc += sq64(x[k].z);
+        acc += sq64(x[k].w);
+      }
+    }
+  }
+  if (SUMSQ) {
+    const double tot = block_sum<kFoldThreads>(acc, red);
+    if (t == 0) slot_sumsq[s] = tot;
+  }
+}
+
+template <typename T>
+hipError_t launch(const SlotPlan* plan, void** srcs, float* dst, double* sumsq, int64_t nslots,
+                  hipStream_t stream) {
+  if (nslots == 0) return hipSuccess;
+  if (sumsq)
+    hipLaunchKernelGGL((fold_kernel<T, true>), dim3(nslots), dim3(kFoldThreads), 0, stream, plan, srcs, dst, sumsq);
+  else
+    hipLaunchKernelGGL((fold_kernel<T, false>), dim3(nslots), dim3(kFoldThreads), 0, stream, plan, srcs, dst,
+                       sumsq);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace fp8z1
+
+using namespace fp8z1;
+
+extern "C" int fp8z1_fold(const fp8z1_table* ct, const void* const* src, int32_t src_dtype, float* dst,
+                          double* slot_sumsq, void* stream) {
+  fp8z1_table* t = const_cast<fp8z1_table*>(ct);
+  if (!t || !src || !dst) return set_error(FP8Z1_EINVAL, "fold: NULL table, src list or dst");
+  if (src_dtype != FP8Z1_F32 && src_dtype != FP8Z1_BF16)
+    return set_error(FP8Z1_EINVAL, "fold: src_dtype must be FP8Z1_F32 or FP8Z1_BF16");
+  const size_t el = src_dtype == FP8Z1_F32 ? 4 : 2;
+  // every param the shard holds needs a source pointer, element-aligned
+  for (const fp8z1_block& e : t->entries) {
+    if (e.param < 0) continue;
+    const void* p = src[e.param];
+    if (!p) return set_error(FP8Z1_EINVAL, "fold: src pointer of param " + std::to_string(e.param) + " is NULL");
+    if (reinterpret_cast<uintptr_t>(p) % el)
+      return set_error(FP8Z1_EINVAL, "fold: src pointer of param " + std::to_string(e.param) + " is misaligned");
+  }
+  if (reinterpret_cast<uintptr_t>(dst) % 16) return set_error(FP8Z1_EINVAL, "fold: dst must be 16-byte aligned");
+  if (slot_sumsq && reinterpret_cast<uintptr_t>(slot_sumsq) % 8)
+    return set_error(FP8Z1_EINVAL, "fold: slot_sumsq must be 8-byte aligned");
+  std::lock_guard<std::mutex> lock(t->mu);
+  int rc = ensure_device(t);
+  if (rc) return rc;
+  void** dsrc = nullptr;
+  rc = device_ptr_list(t, kRoleFoldSrc, src, &dsrc, stream);
+  if (rc) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = src_dtype == FP8Z1_F32
+                     ? launch<float>(t->d_plan, dsrc, dst, slot_sumsq, t->info.shard_slots, st)
+                     : launch<uint16_t>(t->d_plan, dsrc, dst, slot_sumsq, t->info.shard_slots, st);
+  return check_hip(e, "fold: launch");
+}

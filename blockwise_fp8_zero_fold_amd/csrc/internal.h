@@ -1,0 +1,64 @@
+// Internal definitions shared by the fp8z1 library sources (not part of the ABI).
+#pragma once
+
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/fp8z1.h"
+
+namespace fp8z1 {
+
+constexpr int kB = FP8Z1_BLOCK;          // block edge
+constexpr int kBlockElems = kB * kB;     // 16384 elements per block
+
+// Per-slot launch record kept on the device, derived from the 16-byte ABI
+// entry and the param shapes so that a kernel needs one 32-byte load per
+// slot.  `off` is the element offset of the block's (0, 0) element in its
+// param's row-major [E, R, C] buffer, `ld` the row stride C, `soff` the
+// offset of the block's scale in the param's [E, Rb, Cb] scale array.
+struct SlotPlan {
+  int64_t off;
+  int64_t ld;
+  int32_t param;  // -1: padding slot
+  int32_t soff;
+  uint16_t vr, vc;
+  uint32_t pad;
+};
+static_assert(sizeof(SlotPlan) == 32, "SlotPlan is 32 bytes");
+
+enum PtrRole { kRoleFoldSrc = 0, kRoleUnfoldDst = 1, kRoleUnfoldScale = 2, kNumRoles = 3 };
+
+// Device-side pointer list for one role: a pinned host mirror, the device
+// array and an event marking the end of the last upload from the mirror.
+struct PtrCache {
+  const void** host = nullptr;  // pinned
+  void** dev = nullptr;
+  void* done = nullptr;  // hipEvent_t
+  bool valid = false;
+};
+
+}  // namespace fp8z1
+
+struct fp8z1_table {
+  fp8z1_table_info info{};
+  std::vector<fp8z1_shape> shapes;
+  std::vector<fp8z1_block> entries;
+  // device state, created at the first GPU use
+  std::mutex mu;
+  int device = -1;
+  fp8z1::SlotPlan* d_plan = nullptr;
+  fp8z1::PtrCache ptrs[fp8z1::kNumRoles];
+};
+
+namespace fp8z1 {
+
+int set_error(int status, const std::string& msg);
+// Bind the table to the current device and upload its plan (first call only).
+int ensure_device(fp8z1_table* t);
+// Upload (if changed) a host list of n_params device pointers; returns the device array.
+int device_ptr_list(fp8z1_table* t, PtrRole role, const void* const* host_list, void*** out, void* stream);
+int check_hip(int hip_status, const char* what);
+
+}  // namespace fp8z1

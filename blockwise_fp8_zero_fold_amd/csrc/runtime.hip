@@ -1,0 +1,129 @@
+// Device side of a table handle: the per-slot launch plan, the per-param
+// pointer lists, release; and state copies to and from the host.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "internal.h"
+
+namespace fp8z1 {
+
+int check_hip(int hip_status, const char* what) {
+  const hipError_t e = static_cast<hipError_t>(hip_status);
+  if (e == hipSuccess) return FP8Z1_OK;
+  return set_error(FP8Z1_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int ensure_device(fp8z1_table* t) {
+  int dev = -1;
+  int rc = check_hip(hipGetDevice(&dev), "hipGetDevice");
+  if (rc) return rc;
+  if (t->device >= 0) {
+    if (dev != t->device)
+      return set_error(FP8Z1_EDEVICE, "table is bound to device " + std::to_string(t->device) + ", current is " +
+                                           std::to_string(dev));
+    return FP8Z1_OK;
+  }
+  const size_t n = t->entries.size();
+  std::vector<SlotPlan> plan(n);
+  for (size_t s = 0; s < n; ++s) {
+    const fp8z1_block& e = t->entries[s];
+    SlotPlan& p = plan[s];
+    std::memset(&p, 0, sizeof(p));
+    p.param = e.param;
+    if (e.param < 0) continue;
+    const fp8z1_shape& sh = t->shapes[e.param];
+    const int64_t rb = (sh.R + kB - 1) / kB, cb = (sh.C + kB - 1) / kB;
+    p.off = (int64_t(e.expert) * sh.R + int64_t(kB) * e.brow) * sh.C + int64_t(kB) * e.bcol;
+    p.ld = sh.C;
+    p.soff = static_cast<int32_t>((int64_t(e.expert) * rb + e.brow) * cb + e.bcol);
+    p.vr = e.vrows;
+    p.vc = e.vcols;
+  }
+  for (int r = 0; r < kNumRoles; ++r) {
+    PtrCache& c = t->ptrs[r];
+    const size_t bytes = sizeof(void*) * t->shapes.size();
+    rc = check_hip(hipHostMalloc(reinterpret_cast<void**>(&c.host), bytes, hipHostMallocDefault), "hipHostMalloc");
+    if (!rc) rc = check_hip(hipMalloc(reinterpret_cast<void**>(&c.dev), bytes), "hipMalloc");
+    if (!rc) rc = check_hip(hipEventCreateWithFlags(reinterpret_cast<hipEvent_t*>(&c.done), hipEventDisableTiming),
+                            "hipEventCreate");
+    if (rc) return rc;
+    c.valid = false;
+  }
+  if (n) {
+    rc = check_hip(hipMalloc(reinterpret_cast<void**>(&t->d_plan), n * sizeof(SlotPlan)), "hipMalloc(plan)");
+    if (rc) return rc;
+    rc = check_hip(hipMemcpy(t->d_plan, plan.data(), n * sizeof(SlotPlan), hipMemcpyHostToDevice), "hipMemcpy(plan)");
+    if (rc) return rc;
+  }
+  t->device = dev;
+  return FP8Z1_OK;
+}
+
+int device_ptr_list(fp8z1_table* t, PtrRole role, const void* const* host_list, void*** out, void* stream) {
+  PtrCache& c = t->ptrs[role];
+  const size_t bytes = sizeof(void*) * t->shapes.size();
+  if (!c.valid || std::memcmp(c.host, host_list, bytes) != 0) {
+    hipEvent_t ev = static_cast<hipEvent_t>(c.done);
+    if (c.valid) {
+      // the previous upload may still be reading the pinned mirror
+      int rc = check_hip(hipEventSynchronize(ev), "hipEventSynchronize");
+      if (rc) return rc;
+    }
+    std::memcpy(c.host, host_list, bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int rc = check_hip(hipMemcpyAsync(c.dev, c.host, bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync(pointer list)");
+    if (!rc) rc = check_hip(hipEventRecord(ev, s), "hipEventRecord");
+    if (rc) {
+      c.valid = false;
+      return rc;
+    }
+    c.valid = true;
+  }
+  *out = c.dev;
+  return FP8Z1_OK;
+}
+
+}  // namespace fp8z1
+
+using namespace fp8z1;
+
+extern "C" void fp8z1_table_free(fp8z1_table* t) {
+  if (!t) return;
+  bool any = t->d_plan != nullptr;
+  for (int r = 0; r < kNumRoles; ++r) any = any || t->ptrs[r].host || t->ptrs[r].dev || t->ptrs[r].done;
+  if (any) {  // device resources exist only after a GPU call used the table
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (t->device >= 0 && cur != t->device) (void)hipSetDevice(t->device);
+    // pending uploads and kernels that use the table must have finished
+    for (int r = 0; r < kNumRoles; ++r)
+      if (t->ptrs[r].done) (void)hipEventSynchronize(static_cast<hipEvent_t>(t->ptrs[r].done));
+    (void)hipDeviceSynchronize();
+    for (int r = 0; r < kNumRoles; ++r) {
+      PtrCache& c = t->ptrs[r];
+      if (c.host) (void)hipHostFree(c.host);
+      if (c.dev) (void)hipFree(c.dev);
+      if (c.done) (void)hipEventDestroy(static_cast<hipEvent_t>(c.done));
+    }
+    if (t->d_plan) (void)hipFree(t->d_plan);
+    if (t->device >= 0 && cur >= 0 && cur != t->device) (void)hipSetDevice(cur);
+  }
+  delete t;
+}
+
+extern "C" int fp8z1_state_read(const fp8z1_state* d_state, fp8z1_state* out, void* stream) {
+  if (!d_state || !out) return set_error(FP8Z1_EINVAL, "state_read: NULL argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = check_hip(hipMemcpyAsync(out, d_state, sizeof(fp8z1_state), hipMemcpyDeviceToHost, s), "state_read: copy");
+  if (rc) return rc;
+  return check_hip(hipStreamSynchronize(s), "state_read: sync");
+}
+
+extern "C" int fp8z1_state_write(fp8z1_state* d_state, const fp8z1_state* in, void* stream) {
+  if (!d_state || !in) return set_error(FP8Z1_EINVAL, "state_write: NULL argument");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc = check_hip(hipMemcpyAsync(d_state, in, sizeof(fp8z1_state), hipMemcpyHostToDevice, s), "state_write: copy");
+  if (rc) return rc;
+  return check_hip(hipStreamSynchronize(s), "state_write: sync");
+}

@@ -1,0 +1,397 @@
+// The optimizer step on one rank's folded shard, and its state.
+//
+// "面向 Blockwise FP8 量化的 ZeRO 优化器设计", section "总结": after the reduced
+// grads are folded and sliced, the rank updates its FP32 master and then
+// quantizes it into FP8 weights and one scale per 128x128 block.
+// "DeepSpeed ZeRO 优化": step order global norm -> loss-scale update ->
+// unscale/clip -> optimizer step (section 3.2), clip coefficient
+// max_norm / (norm + 1e-6) (section 7), dynamic loss scaling (section 6),
+// overflow = inf/NaN in the grads, which skips the step (section 9, Q6).
+//
+// Kernels, all on the caller's stream, no host synchronization:
+//   K1 sumsq_kernel   one workgroup per slot: float64 sum of squares of the
+//                     slot's real grads -> workspace[slot]   (level 1)
+//   K2 finalize_kernel one workgroup: fixed-order float64 sum of the slot
+//                     sums + the other ranks' sum -> overflow flag, clip and
+//                     unscale factor k, bias-correction scalars, loss scale;
+//                     written to the device state                (level 2)
+//   K3 update_kernel  one workgroup per slot: AdamW on g, p, m, v (16-byte
+//                     loads and stores), the updated block kept in
+//                     registers, block amax (wave shuffles + LDS), scale,
+//                     E4M3 codes.  Returns at once when K2 flagged a skip.
+// K1 is left out when no statistics are needed, or when the fold already
+// wrote the per-slot sums (fused statistics).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "device_util.h"
+#include "e4m3.h"
+
+namespace fp8z1 {
+namespace {
+
+// ---------------------------------------------------------------- K1
+
+__global__ __launch_bounds__(kSumThreads) void sumsq_kernel(const SlotPlan* __restrict__ plan,
+                                                            const float* __restrict__ grad,
+                                                            double* __restrict__ out) {
+  __shared__ double red[kSumThreads / 64];
+  const int64_t s = blockIdx.x;
+  const SlotPlan P = plan[s];
+  const int t = threadIdx.x;
+  double acc = 0.0;
+  if (P.param >= 0) {
+    const float4* g = reinterpret_cast<const float4*>(grad + s * kBlockElems);
+    const int vr = P.vr, vc = P.vc;
+    if (vr == kB && vc == kB) {
+#pragma unroll
+      for (int k = 0; k < kChunks / kSumThreads; ++k) {
+        const float4 x = g[t + kSumThreads * k];
+        acc += sq64(x.x);
+        acc += sq64(x.y);
+        acc += sq64(x.z);
+        acc += sq64(x.w);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kChunks / kSumThreads; ++k) {
+        const int c = t + kSumThreads * k;
+        const int i = c / kChunksPerRow, j = 4 * (c % kChunksPerRow);
+        if (i < vr && j < vc) {
+          const float4 x = g[c];
+          // masked positions add +0, exactly what the fold's zero padding adds
+          acc += j + 0 < vc ? sq64(x.x) : 0.0;
+          acc += j + 1 < vc ? sq64(x.y) : 0.0;
+          acc += j + 2 < vc ? sq64(x.z) : 0.0;
+          acc += j + 3 < vc ? sq64(x.w) : 0.0;
+        } else {
+          acc += 0.0;
+          acc += 0.0;
+          acc += 0.0;
+          acc += 0.0;
+        }
+      }
+    }
+  }
+  const double tot = block_sum<kSumThreads>(acc, red);
+  if (t == 0) out[s] = tot;
+}
+
+// ---------------------------------------------------------------- K2
+
+struct FinalizeArgs {
+  double extra_sumsq;
+  int64_t nslots;
+  float lr, beta1, beta2, weight_decay, max_grad_norm;
+  float growth_factor, backoff_factor;
+  int32_t growth_interval;
+  int32_t loss_scaling;
+  int32_t have_stats;
+  int32_t extra_found_inf;
+};
+
+constexpr int kFinThreads = 256;
+
+__global__ __launch_bounds__(kFinThreads) void finalize_kernel(const double* __restrict__ partial,
+                                                               fp8z1_state* __restrict__ st, FinalizeArgs a) {
+  __shared__ double red[kFinThreads / 64];
+  double acc = 0.0;
+  if (a.have_stats)
+    for (int64_t i = threadIdx.x; i < a.nslots; i += kFinThreads) acc += partial[i];
+  const double local = block_sum<kFinThreads>(acc, red);
+  if (threadIdx.x != 0) return;
+
+  fp8z1_state S = *st;
+  const double scale = a.loss_scaling ? static_cast<double>(S.loss_scale) : 1.0;
+  double glob = 0.0;
+  bool found = false;
+  if (a.have_stats) {
+    glob = local + a.extra_sumsq;
+    found = !isfinite(glob) || a.extra_found_inf != 0;
+  }
+  S.global_sumsq = glob;
+  S.found_inf = found ? 1 : 0;
+  if (found) {
+    S.skipped_total += 1;
+    if (a.loss_scaling) {
+      S.loss_scale = static_cast<float>(scale * static_cast<double>(a.backoff_factor));
+      S.good_steps = 0;
+    }
+    *st = S;
+    return;
+  }
+  double coef = 1.0;
+  if (a.max_grad_norm > 0.0f) {
+    const double norm = sqrt(glob) / scale;
+    const double c = static_cast<double>(a.max_grad_norm) / (norm + 1e-6);
+    if (c < 1.0) coef = c;
+  }
+  S.k = static_cast<float>(coef / scale);
+  S.step += 1;
+  S.beta1_pow = S.beta1_pow * static_cast<double>(a.beta1);
+  S.beta2_pow = S.beta2_pow * static_cast<double>(a.beta2);
+  S.step_size = static_cast<float>(static_cast<double>(a.lr) / (1.0 - S.beta1_pow));
+  S.bc2_sqrt = static_cast<float>(sqrt(1.0 - S.beta2_pow));
+  S.decay = static_cast<float>(1.0 - static_cast<double>(a.lr) * static_cast<double>(a.weight_decay));
+  if (a.loss_scaling) {
+    S.good_steps += 1;
+    if (S.good_steps >= a.growth_interval) {
+      S.loss_scale = static_cast<float>(scale * static_cast<double>(a.growth_factor));
+      S.good_steps = 0;
+    }
+  }
+  *st = S;
+}
+
+__global__ void state_init_kernel(fp8z1_state* st, float loss_scale) {
+  fp8z1_state S;
+  S.step = 0;
+  S.beta1_pow = 1.0;
+  S.beta2_pow = 1.0;
+  S.global_sumsq = 0.0;
+  S.loss_scale = loss_scale;
+  S.k = 1.0f;
+  S.step_size = 0.0f;
+  S.bc2_sqrt = 1.0f;
+  S.decay = 1.0f;
+  S.good_steps = 0;
+  S.found_inf = 0;
+  S.skipped_total = 0;
+  *st = S;
+}
+
+// ---------------------------------------------------------------- K3
+
+struct UpdateArgs {
+  float beta1, beta2, one_minus_beta1, one_minus_beta2, eps;
+};
+
+constexpr int kUpdThreads = 256;
+constexpr int kUpdPasses = kChunks / kUpdThreads;
+
+struct Moments {
+  float p, m, v;
+};
+
+// One element of the AdamW update, one float32 rounding per operation.
+__device__ __forceinline__ Moments adamw1(float g_raw, float p, float m, float v, float k, float decay,
+                                          float step_size, float bc2, const UpdateArgs& a) {
+  const float g = g_raw * k;
+  const float m1 = a.beta1 * m + a.one_minus_beta1 * g;
+  const float v1 = a.beta2 * v + a.one_minus_beta2 * (g * g);
+  const float den = __fsqrt_rn(v1) / bc2 + a.eps;
+  const float p1 = p * decay - step_size * (m1 / den);
+  return {p1, m1, v1};
+}
+
+__device__ __forceinline__ uint32_t pack_codes(float4 x, float s) {
+  return e4m3_encode(x.x / s) | (e4m3_encode(x.y / s) << 8) | (e4m3_encode(x.z / s) << 16) |
+         (e4m3_encode(x.w / s) << 24);
+}
+
+__global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __restrict__ plan,
+                                                             const fp8z1_state* __restrict__ st,
+                                                             const float* __restrict__ grad,
+                                                             float* __restrict__ master, float* __restrict__ mom1,
+                                                             float* __restrict__ mom2, uint8_t* __restrict__ fp8,
+                                                             float* __restrict__ scales, UpdateArgs a) {
+  __shared__ float red[kUpdThreads / 64];
+  if (st->found_inf) return;  // skipped step: nothing changes
+  const float k = st->k, decay = st->decay, step_size = st->step_size, bc2 = st->bc2_sqrt;
+
+  const int64_t s = blockIdx.x;
+  const SlotPlan P = plan[s];
+  const int t = threadIdx.x;
+  uint32_t* codes = reinterpret_cast<uint32_t*>(fp8 + s * kBlockElems);
+  if (P.param < 0) {
+#pragma unroll
+    for (int q = 0; q < kUpdPasses; ++q) codes[t + kUpdThreads * q] = 0u;
+    if (t == 0) scales[s] = 1.0f;
+    return;
+  }
+  const int64_t base = s * (kBlockElems / 4);
+  const float4* g4 = reinterpret_cast<const float4*>(grad) + base;
+  float4* p4 = reinterpret_cast<float4*>(master) + base;
+  float4* m4 = reinterpret_cast<float4*>(mom1) + base;
+  float4* v4 = reinterpret_cast<float4*>(mom2) + base;
+
+  float4 pn[kUpdPasses];
+  float amax = 0.0f;
+  const int vr = P.vr, vc = P.vc;
+  if (vr == kB && vc == kB) {
+#pragma unroll
+    for (int q = 0; q < kUpdPasses; ++q) {
+      const int c = t + kUpdThreads * q;
+      const float4 g = g4[c], p = p4[c], m = m4[c], v = v4[c];
+      const Moments e0 = adamw1(g.x, p.x, m.x, v.x, k, decay, step_size, bc2, a);
+      const Moments e1 = adamw1(g.y, p.y, m.y, v.y, k, decay, step_size, bc2, a);
+      const Moments e2 = adamw1(g.z, p.z, m.z, v.z, k, decay, step_size, bc2, a);
+      const Moments e3 = adamw1(g.w, p.w, m.w, v.w, k, decay, step_size, bc2, a);
+      pn[q] = make_float4(e0.p, e1.p, e2.p, e3.p);
+      p4[c] = pn[q];
+      m4[c] = make_float4(e0.m, e1.m, e2.m, e3.m);
+      v4[c] = make_float4(e0.v, e1.v, e2.v, e3.v);
+      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e0.p), fabsf(e1.p)), fmaxf(fabsf(e2.p), fabsf(e3.p))));
+    }
+  } else {
+    // partial block: padding positions are neither used nor changed (their
+    // loaded values are written back as they were); they count 0 in amax
+#pragma unroll
+    for (int q = 0; q < kUpdPasses; ++q) {
+      const int c = t + kUpdThreads * q;
+      const int i = c / kChunksPerRow, j = 4 * (c % kChunksPerRow);
+      pn[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i < vr && j < vc) {
+        const float4 g = g4[c], p = p4[c], m = m4[c], v = v4[c];
+        float4 np = p, nm = m, nv = v;
+        const float gg[4] = {g.x, g.y, g.z, g.w}, pp[4] = {p.x, p.y, p.z, p.w}, mm[4] = {m.x, m.y, m.z, m.w},
+                    vv[4] = {v.x, v.y, v.z, v.w};
+        float op[4] = {p.x, p.y, p.z, p.w}, om[4] = {m.x, m.y, m.z, m.w}, ov[4] = {v.x, v.y, v.z, v.w};
+        float qn[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (j + e < vc) {
+            const Moments r = adamw1(gg[e], pp[e], mm[e], vv[e], k, decay, step_size, bc2, a);
+            op[e] = r.p;
+            om[e] = r.m;
+            ov[e] = r.v;
+            qn[e] = r.p;
+            amax = fmaxf(amax, fabsf(r.p));
+          }
+        }
+        np = make_float4(op[0], op[1], op[2], op[3]);
+        nm = make_float4(om[0], om[1], om[2], om[3]);
+        nv = make_float4(ov[0], ov[1], ov[2], ov[3]);
+        p4[c] = np;
+        m4[c] = nm;
+        v4[c] = nv;
+        pn[q] = make_float4(qn[0], qn[1], qn[2], qn[3]);
+      }
+    }
+  }
+
+  amax = block_max<kUpdThreads>(amax, red);
+  const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+  if (vr == kB && vc == kB) {
+#pragma unroll
+    for (int q = 0; q < kUpdPasses; ++q) codes[t + kUpdThreads * q] = pack_codes(pn[q], scale);
+  } else {
+#pragma unroll
+    for (int q = 0; q < kUpdPasses; ++q) {
+      const int c = t + kUpdThreads * q;
+      const int i = c / kChunksPerRow, j = 4 * (c % kChunksPerRow);
+      uint32_t w = 0u;
+      if (i < vr && j < vc) {
+        w = pack_codes(pn[q], scale);
+        // padding positions get code 0
+        const int nvalid = vc - j;
+        if (nvalid < 4) w &= (1u << (8 * nvalid)) - 1u;
+      }
+      codes[c] = w;
+    }
+  }
+  if (t == 0) scales[s] = scale;
+}
+
+__global__ void encode_kernel(const float* __restrict__ in, uint8_t* __restrict__ out, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = static_cast<uint8_t>(e4m3_encode(in[i]));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; }
+
+}  // namespace
+}  // namespace fp8z1
+
+using namespace fp8z1;
+
+extern "C" int fp8z1_state_init(const fp8z1_hparams* hp, fp8z1_state* d_state, void* stream) {
+  if (!hp || !d_state) return set_error(FP8Z1_EINVAL, "state_init: NULL argument");
+  if (reinterpret_cast<uintptr_t>(d_state) % 8) return set_error(FP8Z1_EINVAL, "state_init: state must be 8-byte aligned");
+  const float s0 = hp->loss_scaling ? hp->init_scale : 1.0f;
+  if (hp->loss_scaling && !(s0 > 0.0f && std::isfinite(s0)))
+    return set_error(FP8Z1_EINVAL, "state_init: init_scale must be finite and > 0");
+  hipLaunchKernelGGL(state_init_kernel, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream), d_state, s0);
+  return check_hip(hipGetLastError(), "state_init: launch");
+}
+
+extern "C" int fp8z1_step_workspace_bytes(const fp8z1_table* t, size_t* bytes) {
+  if (!t || !bytes) return set_error(FP8Z1_EINVAL, "step_workspace_bytes: NULL argument");
+  *bytes = static_cast<size_t>(t->info.shard_slots) * sizeof(double);
+  return FP8Z1_OK;
+}
+
+extern "C" int fp8z1_step(const fp8z1_table* ct, const fp8z1_hparams* hp, fp8z1_state* d_state, const float* grad,
+                          float* master, float* m, float* v, uint8_t* fp8, float* scales, void* d_workspace,
+                          size_t workspace_bytes, int32_t presummed, void* stream) {
+  fp8z1_table* t = const_cast<fp8z1_table*>(ct);
+  if (!t || !hp || !d_state || !grad || !master || !m || !v || !fp8 || !scales)
+    return set_error(FP8Z1_EINVAL, "step: NULL argument");
+  if (!aligned16(grad) || !aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(fp8))
+    return set_error(FP8Z1_EINVAL, "step: grad, master, m, v and fp8 must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(scales) % 4 || reinterpret_cast<uintptr_t>(d_state) % 8)
+    return set_error(FP8Z1_EINVAL, "step: misaligned scales or state");
+  if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f && hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
+    return set_error(FP8Z1_EINVAL, "step: betas must be in [0, 1)");
+  if (!(hp->eps > 0.0f) || !std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay))
+    return set_error(FP8Z1_EINVAL, "step: eps must be > 0, lr and weight_decay finite");
+  if (hp->loss_scaling && hp->growth_interval < 1)
+    return set_error(FP8Z1_EINVAL, "step: growth_interval must be >= 1");
+  const bool stats = hp->max_grad_norm > 0.0f || hp->loss_scaling != 0;
+  const int64_t n = t->info.shard_slots;
+  if (stats) {
+    if (!d_workspace) return set_error(FP8Z1_EINVAL, "step: statistics need the workspace");
+    if (workspace_bytes < static_cast<size_t>(n) * sizeof(double))
+      return set_error(FP8Z1_EINVAL, "step: workspace smaller than fp8z1_step_workspace_bytes()");
+    if (reinterpret_cast<uintptr_t>(d_workspace) % 8) return set_error(FP8Z1_EINVAL, "step: misaligned workspace");
+  }
+  std::lock_guard<std::mutex> lock(t->mu);
+  int rc = ensure_device(t);
+  if (rc) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  double* partial = static_cast<double*>(d_workspace);
+  if (stats && !presummed && n > 0) {
+    hipLaunchKernelGGL(sumsq_kernel, dim3(n), dim3(kSumThreads), 0, s, t->d_plan, grad, partial);
+    rc = check_hip(hipGetLastError(), "step: statistics launch");
+    if (rc) return rc;
+  }
+  FinalizeArgs fa;
+  fa.extra_sumsq = hp->extra_sumsq;
+  fa.nslots = n;
+  fa.lr = hp->lr;
+  fa.beta1 = hp->beta1;
+  fa.beta2 = hp->beta2;
+  fa.weight_decay = hp->weight_decay;
+  fa.max_grad_norm = hp->max_grad_norm;
+  fa.growth_factor = hp->growth_factor;
+  fa.backoff_factor = hp->backoff_factor;
+  fa.growth_interval = hp->growth_interval;
+  fa.loss_scaling = hp->loss_scaling ? 1 : 0;
+  fa.have_stats = stats ? 1 : 0;
+  fa.extra_found_inf = hp->extra_found_inf ? 1 : 0;
+  hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kFinThreads), 0, s, partial, d_state, fa);
+  rc = check_hip(hipGetLastError(), "step: finalize launch");
+  if (rc) return rc;
+  if (n == 0) return FP8Z1_OK;
+  UpdateArgs ua;
+  ua.beta1 = hp->beta1;
+  ua.beta2 = hp->beta2;
+  ua.one_minus_beta1 = static_cast<float>(1.0 - static_cast<double>(hp->beta1));
+  ua.one_minus_beta2 = static_cast<float>(1.0 - static_cast<double>(hp->beta2));
+  ua.eps = hp->eps;
+  hipLaunchKernelGGL(update_kernel, dim3(n), dim3(kUpdThreads), 0, s, t->d_plan, d_state, grad, master, m, v, fp8,
+                     scales, ua);
+  return check_hip(hipGetLastError(), "step: update launch");
+}
+
+extern "C" int fp8z1_encode_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
+  if (n < 0 || (n > 0 && (!in || !out))) return set_error(FP8Z1_EINVAL, "encode_e4m3: bad arguments");
+  if (n == 0) return FP8Z1_OK;
+  const int threads = 256;
+  const int64_t blocks = (n + threads - 1) / threads;
+  if (blocks > 0x7fffffff) return set_error(FP8Z1_EINVAL, "encode_e4m3: n too large for one launch");
+  hipLaunchKernelGGL(encode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0,
+                     static_cast<hipStream_t>(stream), in, out, n);
+  return check_hip(hipGetLastError(), "encode_e4m3: launch");
+}

@@ -80,7 +80,7 @@ def run_sharded_all_ranks(w, steps: int = None, ranks=None) -> Dict[int, List[di
             st, mas, m, v, c, sc = step.step_sharded(tabs[r], w.hp, s["st"], gf[r], s["master"], s["m"], s["v"],
                                                      s["codes"], s["scales"], extra_sumsq=extra)
             state[r] = dict(st=st, master=mas, m=m, v=v, codes=c, scales=sc)
-            out[r].append(dict(state=st, master=mas, m=m, v=v, codes=c, scales=sc, grad=gf[r]))
+            out[r].append(dict(state=st, master=mas, m=m, v=v, codes=c, scales=sc, grad=gf[r], extra=extra))
     return out, tabs
 
 

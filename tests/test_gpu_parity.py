@@ -1,0 +1,313 @@
+"""GPU parity: the HIP path through the C-ABI against the oracle, element by element,
+on seeded inputs that span several blocks, ragged tails, padding slots, clipping,
+loss scaling and a skipped step."""
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import e4m3 as oe4m3
+from oracle import layout, optim, table as otable
+from tests import harness
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+fz = None
+
+
+def setup_module(module):
+    global fz
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import blockwise_fp8_zero_fold_amd as _fz  # raises if the library is not built
+    fz = _fz
+    from tests import gpu_harness  # noqa: F401
+
+
+def _gh():
+    from tests import gpu_harness
+    return gpu_harness
+
+
+# ---------------------------------------------------------------- encoder
+
+def test_encoder_exhaustive_vs_torch_cast():
+    """All 2^32 float32 patterns: the device encoder equals torch's E4M3FN cast after
+    clamping to +-448 (NaN codes checked against the sign rule)."""
+    chunk = 1 << 28
+    out = torch.empty(chunk, dtype=torch.uint8, device="cuda")
+    for i in range(16):
+        lo = -(1 << 31) + i * chunk
+        u = torch.arange(lo, lo + chunk, dtype=torch.int32, device="cuda")
+        x = u.view(torch.float32)
+        fz.fp8z1_encode_e4m3(x, out)
+        ref = x.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+        nan = torch.isnan(x)
+        bad = (out != ref) & ~nan
+        assert int(bad.sum()) == 0, f"chunk {i}: {int(bad.sum())} mismatches"
+        want_nan = torch.where(u < 0, 0xFF, 0x7F).to(torch.uint8)
+        assert bool(((out == want_nan) | ~nan).all())
+    torch.cuda.synchronize()
+
+
+def test_encoder_matches_oracle_sample():
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 2 ** 32, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    # every exponent x every pattern of the top 5 mantissa bits x a few low-bit patterns x both signs
+    e = np.arange(256, dtype=np.uint32)[:, None, None]
+    m = (np.arange(32, dtype=np.uint32) << 18)[None, :, None]
+    low = np.array([0, 1, 0x1FFFF, 0x20000, 0x3FFFF, 0x12345], dtype=np.uint32)[None, None, :]
+    grid = ((e << 23) | m | low).ravel()
+    bits = np.concatenate([bits, grid, grid | np.uint32(0x80000000)])
+    x = bits.view(np.float32)
+    xd = torch.from_numpy(x.copy()).cuda()
+    out = torch.empty(len(x), dtype=torch.uint8, device="cuda")
+    fz.fp8z1_encode_e4m3(xd, out)
+    got = out.cpu().numpy()
+    want = oe4m3.encode(x)
+    assert (got == want).all(), np.nonzero(got != want)[0][:5]
+
+
+# ---------------------------------------------------------------- fold / unfold
+
+SMALL = ["tiny", "dense_small", "moe_small", "ragged_small", "full_small"]
+
+
+@pytest.mark.parametrize("name", SMALL)
+@pytest.mark.parametrize("split", [0, 1])
+def test_fold_unfold_bit_exact(name, split):
+    gh = _gh()
+    w = synth.get(name)
+    rng = np.random.default_rng(9)
+    # random bit patterns: NaN payloads, -0, subnormals must all move unchanged
+    src = {p: rng.integers(0, 2 ** 32, size=s, dtype=np.uint64).astype(np.uint32).view(np.float32)
+           for p, s in enumerate(w.shapes)}
+    src16 = {p: rng.integers(0, 2 ** 16, size=s, dtype=np.uint16) for p, s in enumerate(w.shapes)}
+    for r in list(range(w.dp))[:4] + [otable.ALL_RANKS]:
+        tab = otable.build(w.shapes, w.dp, r, split)
+        t = fz.fp8z1_build_table(w.shapes, w.dp, r, split)
+        n = t.shard_slots
+        held = gh.held_experts(tab["entries"])
+        d32 = [torch.from_numpy(src[p]).cuda() if p in held else None for p in range(w.n_params)]
+        d16 = [torch.from_numpy(src16[p].view(np.int16)).cuda().view(torch.bfloat16) if p in held else None
+               for p in range(w.n_params)]
+        dst = torch.full((n * 16384,), float("nan"), dtype=torch.float32, device="cuda")
+        fz.fp8z1_fold(t, d32, fz.F32, dst)
+        want = layout.fold_shard(tab, src)
+        assert gh.bits_equal(gh.folded(dst, n), want), (r, gh.first_diff(gh.folded(dst, n), want))
+        # unfold into sentinel-filled arrays: held positions get the source bits back, the rest is untouched
+        sentinel = np.uint32(0x7FC0DEAD)
+        outs = [torch.full(s, 0, dtype=torch.int32, device="cuda").fill_(int(sentinel)).view(torch.float32)
+                if p in held else None for p, s in enumerate(w.shapes)]
+        fz.fp8z1_unfold(t, dst, fz.F32, None, outs)
+        ones = layout.valid_mask(tab)
+        for p in held:
+            mask = np.zeros(w.shapes[p], bool)
+            layout.unfold_shard(tab, ones, {p: mask, **{q: np.zeros(w.shapes[q], bool) for q in held if q != p}})
+            got = outs[p].cpu().numpy().view(np.uint32)
+            assert (got[mask] == src[p].view(np.uint32)[mask]).all(), (r, p)
+            assert (got[~mask] == sentinel).all(), (r, p)
+        # bf16 fold widens exactly
+        dst.fill_(float("nan"))
+        fz.fp8z1_fold(t, d16, fz.BF16, dst)
+        want16 = layout.fold_shard(tab, {p: layout.widen_bf16(src16[p]) for p in held})
+        assert gh.bits_equal(gh.folded(dst, n), want16), (r, "bf16")
+        t.free()
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged_small", "moe_small"])
+def test_fused_statistics_equal_separate_kernel(name):
+    """Per-slot sums of squares written by the fold equal the separate statistics
+    kernel's bit for bit, and the oracle's per-slot float64 sums to 1e-12."""
+    gh = _gh()
+    w = synth.get(name)
+    hp = fz.Hparams.make(synth.Hparams(max_grad_norm=1.0))
+    for r in range(min(w.dp, 4)):
+        from blockwise_fp8_zero_fold_amd.shard import Shard
+        sh = Shard(w.shapes, w.dp, r)
+        tab = otable.build(w.shapes, w.dp, r)
+        held = gh.held_experts(tab["entries"])
+        g = gh.grad_tensors(w, held, 1)
+        sh.init(hp, gh.master_tensors(w, held), fz.BF16 if w.master_dtype == "bf16" else fz.F32)
+        sh.fold_grads(hp, g, fused_stats=True)
+        fused = sh.workspace.cpu().numpy().copy()
+        sh.update(hp, presummed=False)  # recomputes the sums with the statistics kernel
+        sep = sh.workspace.cpu().numpy()
+        assert fused.tobytes() == sep.tobytes()
+        gf = layout.fold_shard(tab, harness.grads(w, 1))
+        mask = layout.valid_mask(tab)
+        want = np.array([optim.local_sumsq(gf[s][mask[s]]) for s in range(len(mask))])
+        assert np.all(np.abs(fused[:len(want)] - want) <= 1e-12 * np.abs(want))
+
+
+# ---------------------------------------------------------------- the step
+
+def _bar(got, want, what):
+    """The parity bar: float32 state within 1e-6 relative (with a floor of 1e-6*|lr| for
+    values that cancel to near 0), exact equality expected."""
+    g = got.astype(np.float64)
+    x = want.astype(np.float64)
+    both_nan = np.isnan(g) & np.isnan(x)
+    ok = both_nan | (np.abs(g - x) <= 1e-6 * np.abs(x) + 1e-9)
+    assert ok.all(), f"{what}: {int((~ok).sum())} elements outside 1e-6 relative"
+
+
+def _codes_bar(got, want, what):
+    d = oe4m3.ulp_distance(got, want)
+    assert d.max() <= 1, f"{what}: code distance {d.max()}"
+    assert (d > 0).mean() <= 1e-4, f"{what}: {(d > 0).mean()} of codes differ by 1 ulp"
+
+
+def _run_parity(w, ranks=None, fused=None):
+    gh = _gh()
+    from blockwise_fp8_zero_fold_amd.shard import Shard
+    ranks = w.ranks if ranks is None else ranks
+    ref, tabs = harness.run_sharded_all_ranks(w, ranks=ranks)
+    un = harness.run_unsharded(w)
+    split = fz.SPLIT_PARAM if w.split == "param" else fz.SPLIT_BLOCK
+    dtype = fz.BF16 if w.master_dtype == "bf16" else fz.F32
+    P0 = harness.masters(w)
+    for r in ranks:
+        tab = tabs[r]
+        sh = Shard(w.shapes, w.dp, r, split)
+        n = sh.n_slots
+        held = gh.held_experts(tab["entries"])
+        sh.init(fz.Hparams.make(w.hp), gh.master_tensors(w, held), dtype)
+        assert gh.bits_equal(gh.folded(sh.master, n), layout.fold_shard(tab, P0)), "init fold"
+        codes, scales = gh.code_tensors(w, held)
+        mask = layout.valid_mask(tab)
+        heldmask = {p: np.zeros(s, bool) for p, s in enumerate(w.shapes)}
+        layout.unfold_shard(tab, mask, heldmask)
+        blockmask = {p: np.zeros(otable.grid(s), bool) for p, s in enumerate(w.shapes)}
+        for e in tab["entries"]:
+            if e["param"] >= 0:
+                blockmask[int(e["param"])][int(e["expert"]), int(e["brow"]), int(e["bcol"])] = True
+        for t in range(1, w.steps + 1):
+            R = ref[r][t - 1]
+            hp = fz.Hparams.make(w.hp, extra_sumsq=R["extra"])
+            use_fused = (t % 2 == 0) if fused is None else fused
+            sh.step(hp, gh.grad_tensors(w, held, t), codes, scales, fused_stats=use_fused)
+            torch.cuda.synchronize()
+            tag = f"{w.name} rank {r} step {t}"
+            assert gh.bits_equal(gh.folded(sh.grad, n), R["grad"]), f"{tag}: grad fold"
+            st = sh.read_state()
+            want_st = R["state"]
+            for key in ("step", "found_inf", "skipped_total", "good_steps"):
+                assert st[key] == want_st[key], (tag, key, st[key], want_st[key])
+            for key in ("k", "loss_scale", "step_size", "bc2_sqrt", "decay", "beta1_pow", "beta2_pow"):
+                assert st[key] == want_st[key], (tag, key, st[key], want_st[key])
+            if want_st["global_sumsq"] != 0 or st["global_sumsq"] != 0:
+                a, b = st["global_sumsq"], want_st["global_sumsq"]
+                assert (np.isinf(a) and np.isinf(b)) or abs(a - b) <= 1e-12 * abs(b), (tag, a, b)
+            for name, dt in (("master", np.float32), ("m", np.float32), ("v", np.float32)):
+                got = gh.folded(getattr(sh, name), n)
+                _bar(got[mask], R[name][mask], f"{tag}: {name}")
+                assert gh.bits_equal(got, R[name]), f"{tag}: {name} not bit-exact {gh.first_diff(got, R[name])}"
+            got_codes = gh.folded(sh.fp8, n, np.uint8)
+            _codes_bar(got_codes[mask], R["codes"][mask], f"{tag}: codes")
+            assert gh.bits_equal(got_codes, R["codes"]), f"{tag}: codes not bit-exact"
+            got_sc = sh.scales.cpu().numpy()[:n]
+            _bar(got_sc, R["scales"], f"{tag}: scales")
+            assert gh.bits_equal(got_sc, R["scales"]), f"{tag}: scales not bit-exact"
+            U = un[t - 1]
+            if U["codes"] is not None:
+                for p in held:
+                    c = codes[p].cpu().numpy()
+                    assert (c[heldmask[p]] == U["codes"][p][heldmask[p]]).all(), f"{tag}: unfolded codes p{p}"
+                    assert (c[~heldmask[p]] == 0xA5).all(), f"{tag}: unfold wrote outside the shard p{p}"
+                    s = scales[p].cpu().numpy()
+                    assert gh.bits_equal(s[blockmask[p]], U["scales"][p][blockmask[p]]), f"{tag}: scales p{p}"
+                    assert np.isnan(s[~blockmask[p]]).all()
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_clip", "tiny_lossscale", "dense_small", "moe_small", "full_small"])
+def test_step_parity(name):
+    _run_parity(synth.get(name))
+
+
+@pytest.mark.parametrize("split", ["block", "param"])
+def test_step_parity_ragged(split):
+    w = synth.get("ragged_small").with_(split=split)
+    _run_parity(w, ranks=[0, 5, 7, 15])
+
+
+def test_padding_poison_gpu():
+    """NaN in the folded grad padding and NaN-payload sentinels in master/m/v padding:
+    the step masks by the table, so no skip, sentinels unchanged, results as clean."""
+    gh = _gh()
+    from blockwise_fp8_zero_fold_amd.shard import Shard
+    w = synth.get("tiny_clip")
+    tab = otable.build(w.shapes, w.dp, 1)
+    mask = torch.from_numpy(layout.valid_mask(tab).reshape(-1)).cuda()
+    held = gh.held_experts(tab["entries"])
+    hp = fz.Hparams.make(w.hp, extra_sumsq=0.0)
+    res = []
+    for poison in (False, True):
+        sh = Shard(w.shapes, w.dp, 1)
+        sh.init(hp, gh.master_tensors(w, held))
+        sh.fold_grads(hp, gh.grad_tensors(w, held, 1), fused_stats=False)
+        if poison:
+            sent = torch.tensor([0x7FC0BEEF], dtype=torch.int32, device="cuda").view(torch.float32)
+            sh.grad[~mask] = float("nan")
+            for b in (sh.master, sh.m, sh.v):
+                b[~mask] = sent
+        sh.update(hp, presummed=False)
+        torch.cuda.synchronize()
+        res.append(sh)
+    clean, dirty = res
+    assert dirty.read_state()["found_inf"] == 0
+    for name in ("master", "m", "v"):
+        a, b = getattr(clean, name), getattr(dirty, name)
+        assert torch.equal(a[mask].view(torch.int32), b[mask].view(torch.int32))
+        assert bool((b[~mask].view(torch.int32) == 0x7FC0BEEF).all())
+    assert torch.equal(clean.fp8, dirty.fp8) and torch.equal(clean.scales, dirty.scales)
+    assert int(dirty.fp8[~mask].sum()) == 0
+
+
+def test_determinism_and_resume():
+    """Two runs give identical bits; 2 steps + save/restore + 3 steps equals 5 steps."""
+    gh = _gh()
+    from blockwise_fp8_zero_fold_amd.shard import Shard
+    w = synth.get("tiny_lossscale")
+    tab = otable.build(w.shapes, w.dp, 1)
+    held = gh.held_experts(tab["entries"])
+    hp = fz.Hparams.make(w.hp)
+    grads = [gh.grad_tensors(w, held, t) for t in range(1, 6)]
+
+    def run(steps, sh=None):
+        if sh is None:
+            sh = Shard(w.shapes, w.dp, 1)
+            sh.init(hp, gh.master_tensors(w, held))
+        codes, scales = gh.code_tensors(w, held)
+        for t in steps:
+            sh.step(hp, grads[t - 1], codes, scales)
+        torch.cuda.synchronize()
+        return sh
+
+    a = run(range(1, 6))
+    b = run(range(1, 6))
+    for name in ("master", "m", "v", "fp8", "scales", "state"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    c = run(range(1, 3))
+    saved = {name: getattr(c, name).clone() for name in ("master", "m", "v", "fp8", "scales")}
+    st = c.read_state()
+    d = Shard(w.shapes, w.dp, 1)
+    for name, x in saved.items():
+        getattr(d, name).copy_(x)
+    fz.fp8z1_state_write(d.state, st)
+    d = run(range(3, 6), d)
+    for name in ("master", "m", "v", "fp8", "scales"):
+        assert torch.equal(getattr(a, name), getattr(d, name)), name
+    assert a.read_state() == d.read_state()
+
+
+def test_empty_and_degenerate_blocks():
+    """All-zero weights and grads (amax 0 -> scale 1, codes 0), a block of one element,
+    and a 1x1 param."""
+    gh = _gh()
+    from blockwise_fp8_zero_fold_amd.shard import Shard
+    w = synth.Workload(name="degen", shapes=((1, 1, 1), (1, 129, 1), (2, 1, 130)), dp=3, ranks=(0, 1, 2), steps=2,
+                       hp=synth.Hparams(max_grad_norm=1.0), grad_sigma=0.0, master_sigma=0.0)
+    _run_parity(w)

@@ -1,0 +1,122 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared symbol, and its
+host-only table builder is byte-identical to the oracle's table.  No GPU calls."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import table as otable
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8z1.h")
+
+fz = pytest.importorskip("blockwise_fp8_zero_fold_amd", reason="libfp8z1.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8z1_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert "fp8z1_step" in names and len(names) >= 14
+    for n in names:
+        assert hasattr(fz.lib, n), n
+    # the symbols are plain C names (no C++ mangling)
+    nm = os.popen(f"nm -D --defined-only {fz.lib_path}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}$", nm, flags=re.M), n
+
+
+def _cmp(w_shapes, dp, rank, split):
+    t = fz.fp8z1_build_table(w_shapes, dp, rank, split)
+    o = otable.build(w_shapes, dp, rank, split)
+    assert t.entries().tobytes() == o["entries"].tobytes()
+    for k in ("split", "dp", "rank", "slots_per_rank", "total_blocks", "shard_first_slot", "shard_slots",
+              "valid_elems", "pad_elems"):
+        assert t.info[k] == o[k], k
+    assert t.info["n_params"] == len(w_shapes)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_clip", "dense_small", "moe_small", "ragged_small", "full_small"])
+@pytest.mark.parametrize("split", [0, 1])
+def test_table_matches_oracle_all_ranks(name, split):
+    w = synth.get(name)
+    for r in list(range(w.dp)) + [otable.ALL_RANKS]:
+        _cmp(w.shapes, w.dp, r, split)
+
+
+@pytest.mark.parametrize("name,rank", [("dense", 3), ("moe", 5), ("full", 0), ("ragged", 7), ("ragged", 15)])
+@pytest.mark.parametrize("split", [0, 1])
+def test_table_matches_oracle_full_size(name, rank, split):
+    w = synth.get(name)
+    _cmp(w.shapes, w.dp, rank, split)
+
+
+def test_random_tables_match_oracle():
+    rng = np.random.default_rng(21)
+    for _ in range(40):
+        n = int(rng.integers(1, 12))
+        shapes = [(int(rng.integers(1, 4)), int(rng.integers(1, 600)), int(rng.integers(1, 600))) for _ in range(n)]
+        dp = int(rng.integers(1, 9))
+        for split in (0, 1):
+            _cmp(shapes, dp, int(rng.integers(0, dp)), split)
+
+
+def test_build_table_rejects_bad_arguments():
+    good = [(1, 128, 128)]
+    bad_cases = [
+        (good, 0, 0, 0),        # dp < 1
+        (good, 2, 2, 0),        # rank >= dp
+        (good, 2, -2, 0),       # rank < -1
+        (good, 2, 0, 7),        # unknown split
+        ([(1, 0, 128)], 1, 0, 0),  # empty dimension
+        ([(1, 1 << 23, 128)], 1, 0, 0),  # R too large for the 16-bit block row
+    ]
+    for shapes, dp, rank, split in bad_cases:
+        with pytest.raises(fz.Fp8z1Error):
+            fz.fp8z1_build_table(shapes, dp, rank, split)
+    out = ctypes.c_void_p()
+    assert fz.lib.fp8z1_build_table(None, 0, 1, 0, 0, ctypes.byref(out)) == -1
+    assert out.value is None
+    assert b"n_params" in fz.lib.fp8z1_last_error()
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert fz.lib.fp8z1_status_string(code)
+    assert fz.lib.fp8z1_status_string(-99) == b"unknown status"
+
+
+def test_argument_errors_before_any_gpu_work():
+    """Calls with bad arguments fail in the host checks and never reach HIP."""
+    t = fz.fp8z1_build_table([(1, 256, 256)], 1, 0)
+    hp = fz.Hparams.make(synth.Hparams())
+    with pytest.raises(fz.Fp8z1Error, match="NULL"):
+        fz.fp8z1_fold(t, [None], fz.F32, 16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="src_dtype"):
+        fz.fp8z1_fold(t, [16], 9, 16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="misaligned"):
+        fz.fp8z1_fold(t, [18], fz.F32, 16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="NULL"):
+        fz.fp8z1_step(t, hp, 16, 16, 16, 16, None, 16, 16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="16-byte"):
+        fz.fp8z1_step(t, hp, 16, 16, 16, 16, 24, 16, 16, stream=0)
+    hp_clip = fz.Hparams.make(synth.Hparams(max_grad_norm=1.0))
+    with pytest.raises(fz.Fp8z1Error, match="workspace"):
+        fz.fp8z1_step(t, hp_clip, 16, 16, 16, 16, 16, 16, 16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="workspace"):
+        fz.fp8z1_step(t, hp_clip, 16, 16, 16, 16, 16, 16, 16, workspace=16, workspace_bytes=8, stream=0)
+    hp_bad = fz.Hparams.make(synth.Hparams(beta1=1.0))
+    with pytest.raises(fz.Fp8z1Error, match="betas"):
+        fz.fp8z1_step(t, hp_bad, 16, 16, 16, 16, 16, 16, 16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="dtype"):
+        fz.fp8z1_unfold(t, 16, fz.BF16, None, [16], stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="NULL"):
+        fz.fp8z1_unfold(t, 16, fz.E4M3, None, [None], stream=0)
+    t.free()
