@@ -148,7 +148,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="moe", choices=["moe", "dense", "full", "ragged"])
     ap.add_argument("--unfused-stats", action="store_true", help="separate statistics kernel instead of fold-fused")
-    ap.add_argument("--cpu-slots", type=int, default=2048, help="oracle sample size (slots) for cpu_baseline")
+    ap.add_argument("--cpu-slots", type=int, default=16384, help="oracle sample size (slots) for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:

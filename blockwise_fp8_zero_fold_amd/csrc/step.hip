@@ -180,7 +180,10 @@ __device__ __forceinline__ Moments adamw1(float g_raw, float p, float m, float v
   const float g = g_raw * k;
   const float m1 = a.beta1 * m + a.one_minus_beta1 * g;
   const float v1 = a.beta2 * v + a.one_minus_beta2 * (g * g);
-  const float den = __fsqrt_rn(v1) / bc2 + a.eps;
+  // __builtin_sqrtf lowers to the correctly rounded sequence (hardware sqrt,
+  // then a one-ulp correction from the fma residuals); __fsqrt_rn lowers to the
+  // bare hardware sqrt here, which is off by one ulp on some inputs.
+  const float den = __builtin_sqrtf(v1) / bc2 + a.eps;
   const float p1 = p * decay - step_size * (m1 / den);
   return {p1, m1, v1};
 }
