@@ -2,20 +2,24 @@
 """Throughput of the blockwise-FP8 ZeRO-1 shard step on one MI355X.
 
 One step = the whole per-step path on one rank's shard: fold of the reduced
-row-major FP32 grads (with the per-slot sums of squares fused in when
-statistics are on) -> statistics finalize -> AdamW + per-block amax + E4M3
-requant -> unfold of the FP8 codes and scales to row-major.  Inputs (row-major
-grads, folded master/m/v, state) are resident in HBM before timing starts.
+row-major FP32 grads -> statistics (when clipping or loss scaling is on) ->
+finalize -> AdamW + per-block amax + E4M3 requant -> unfold of the FP8 codes
+and scales to row-major.  Headline route (default): the update reads the
+row-major grads itself (the grad fold happens on read, no folded grad copy);
+the route with a separate fold kernel is timed in the same run and reported
+under `alt_mode`.  Inputs (row-major grads, folded master/m/v, state) are
+resident in HBM before timing starts.
 
 Default workload: the MoE expert shard -- params [64,2048,7168] x2 and
 [64,7168,2048] FP32, block-wise split over DP = 8, rank 5 (352,321,536 real
 elements), grads N(0,1e-4) x lognormal(0,1) per expert, no clipping.
 
 Prints one JSON line (rank 0).  `value` = real elements of the shard updated
-per second.  `roofline` is for the dominant call (fp8z1_step: the update
-kernel plus its one-workgroup finalize kernel), timed with HIP events on the
-stream the kernels run on; `cpu_baseline` is the numpy oracle on a bounded
-sample of the same shard.
+per second.  `roofline` is for the dominant call (fp8z1_step_rowmajor or
+fp8z1_step: the update kernel plus its one-workgroup finalize kernel, and the
+statistics pass when one runs), timed with HIP events on the stream the
+kernels run on; `cpu_baseline` is the numpy oracle on a bounded sample of the
+same shard.
 """
 from __future__ import annotations
 
@@ -95,10 +99,11 @@ def _source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(workload: str, src_hash: str):
-    """HBM bytes per fp8z1_step launch from the committed rocprofv3 counter summary,
-    or None when the kernels changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"update_kernel_{workload}_pmc.json")
+def _traffic(workload: str, mode: str, src_hash: str):
+    """HBM bytes (read + written) per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, or None when the kernels changed since the counters
+    were taken."""
+    path = os.path.join(ROOT, "profiles", f"update_kernel_{workload}_{mode}_pmc.json")
     if not os.path.exists(path):
         return None
     try:
@@ -147,9 +152,16 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="moe", choices=["moe", "dense", "full", "ragged"])
+    ap.add_argument("--mode", default="fold_on_read", choices=["fold_on_read", "fold"],
+                    help="headline route: the update reads the row-major grads (fold on read), or a separate "
+                         "fold kernel writes folded grads first; the other route is timed too and reported "
+                         "under alt_mode")
     ap.add_argument("--unfused-stats", action="store_true", help="separate statistics kernel instead of fold-fused")
     ap.add_argument("--cpu-slots", type=int, default=16384, help="oracle sample size (slots) for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run torch's plain copy of 2 x 1 GiB five times (the reference kernel whose "
+                         "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic of the step kernels)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -157,6 +169,17 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.calibrate_copy:
+        n = 1 << 28  # 1 GiB of float32
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy": {"bytes_read_per_launch": 4 * n, "bytes_written_per_launch": 4 * n,
+                                             "launches": 5}}), flush=True)
+        return 0
 
     import blockwise_fp8_zero_fold_amd as fz
     from blockwise_fp8_zero_fold_amd.shard import Shard
@@ -192,38 +215,65 @@ def main() -> int:
           file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        sh.step(hp, grads, codes, scales, fused_stats=fused)
-    torch.cuda.synchronize()
 
-    ev = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(args.steps)],
-              [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]) for k in ("fold", "step", "unfold")}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev["fold"][0][i].record(stream)
-        pre = sh.fold_grads(hp, grads, fused_stats=fused)
-        ev["fold"][1][i].record(stream)
-        ev["step"][0][i].record(stream)
-        sh.update(hp, presummed=pre)
-        ev["step"][1][i].record(stream)
-        ev["unfold"][0][i].record(stream)
+    def one_step(mode, ev=None, i=0):
+        def rec(name, which):
+            if ev is not None:
+                ev[name][which][i].record(stream)
+        if mode == "fold_on_read":
+            rec("step", 0)
+            sh.update_rowmajor(hp, grads)
+            rec("step", 1)
+        else:
+            rec("fold", 0)
+            pre = sh.fold_grads(hp, grads, fused_stats=fused)
+            rec("fold", 1)
+            rec("step", 0)
+            sh.update(hp, presummed=pre)
+            rec("step", 1)
+        rec("unfold", 0)
         sh.unfold(codes, scales)
-        ev["unfold"][1][i].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in zip(*ev[k])])) for k in ev}
-    st = sh.read_state()
-    print(f"# timed {args.steps} steps in {elapsed:.3f}s; per call ms: {ms}; state step {st['step']}",
-          file=sys.stderr, flush=True)
+        rec("unfold", 1)
 
-    ms_per_step = elapsed * 1e3 / args.steps
-    upd_bytes = BYTES_UPDATE * valid + SLOT_BYTES_UPDATE * nslots
-    step_bytes = ((BYTES_FOLD_F32 * valid + SLOT_BYTES_FOLD * nslots) + upd_bytes
-                  + (BYTES_STATS * valid if stats and not fused else 0)
-                  + BYTES_UNFOLD_E4M3 * valid + SLOT_BYTES_UNFOLD * nslots)
-    achieved = upd_bytes / (ms["step"] * 1e-3) / 1e9
+    def timed(mode):
+        for _ in range(args.warmup):
+            one_step(mode)
+        torch.cuda.synchronize()
+        calls = ("step", "unfold") if mode == "fold_on_read" else ("fold", "step", "unfold")
+        ev = {k: ([torch.cuda.Event(enable_timing=True) for _ in range(args.steps)],
+                  [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]) for k in calls}
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            one_step(mode, ev, i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        ms = {k: float(np.mean([a.elapsed_time(b) for a, b in zip(*ev[k])])) for k in ev}
+        print(f"# {mode}: {args.steps} steps in {elapsed:.3f}s; per call ms: {ms}", file=sys.stderr, flush=True)
+        return elapsed * 1e3 / args.steps, ms
+
+    def step_bytes(mode):
+        """Algorithmic bytes of one whole step, and of its fp8z1_step* call."""
+        call = BYTES_UPDATE * valid + SLOT_BYTES_UPDATE * nslots
+        if stats and (mode == "fold_on_read" or not fused):
+            call += BYTES_STATS * valid + SLOT_BYTES_FOLD * nslots
+        total = call + BYTES_UNFOLD_E4M3 * valid + SLOT_BYTES_UNFOLD * nslots
+        if mode == "fold":
+            total += BYTES_FOLD_F32 * valid + SLOT_BYTES_FOLD * nslots
+        return total, call
+
+    modes = [args.mode, "fold" if args.mode == "fold_on_read" else "fold_on_read"]
+    results = {m: timed(m) for m in modes}
+    st = sh.read_state()
+    print(f"# state step {st['step']}", file=sys.stderr, flush=True)
+
+    ms_per_step, ms = results[args.mode]
+    total_bytes, call_bytes = step_bytes(args.mode)
+    achieved = call_bytes / (ms["step"] * 1e-3) / 1e9
     src_hash = _source_hash()
+    alt_mode = modes[1]
+    alt_ms, alt_calls = results[alt_mode]
+    alt_total, _ = step_bytes(alt_mode)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -250,24 +300,31 @@ def main() -> int:
         "config": {
             "workload": {"moe": "moe_expert_shard", "dense": "dense_layer_set", "full": "full_step_bf16",
                          "ragged": "ragged_600_params"}[w.name],
-            "shapes": [list(s) for s in w.shapes], "dp": w.dp, "rank": rank,
-            "split": w.split, "shard_slots": nslots, "valid_elems": valid,
+            "shapes": [list(s) for s in w.shapes] if len(w.shapes) <= 8 else f"{len(w.shapes)} params",
+            "dp": w.dp, "rank": rank, "split": w.split, "shard_slots": nslots, "valid_elems": valid,
             "clip": w.hp.max_grad_norm, "loss_scaling": bool(w.hp.loss_scaling),
-            "stats": "fused-in-fold" if fused else ("separate" if stats else "off"),
+            "grad_fold": "on read, inside the update" if args.mode == "fold_on_read" else "separate fold kernel",
+            "stats": ("off" if not stats else
+                      "separate pass over row-major grads" if args.mode == "fold_on_read" else
+                      "fused into the fold" if fused else "separate pass over folded grads"),
         },
-        "gbs_algorithmic": step_bytes / (ms_per_step * 1e-3) / 1e9,
-        "hbm_frac_step": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "step_bytes": total_bytes,
+        "gbs_algorithmic": total_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac_step": total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "per_call_ms": ms,
         "roofline": {
-            "kernel": "fp8z1_step (update_kernel + finalize_kernel)",
+            "kernel": "update_kernel" + ("<rowmajor>" if args.mode == "fold_on_read" else "<folded>")
+                      + " + finalize_kernel" + (" + statistics pass" if stats and (args.mode == "fold_on_read" or not fused) else ""),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": _traffic(w.name, src_hash),
-            "bytes_per_launch": upd_bytes,
+            "traffic": _traffic(w.name, args.mode, src_hash),
+            "bytes_per_launch": call_bytes,
         },
+        "alt_mode": {"mode": alt_mode, "ms_per_step": alt_ms, "value": valid / (alt_ms * 1e-3),
+                     "per_call_ms": alt_calls, "gbs_algorithmic": alt_total / (alt_ms * 1e-3) / 1e9},
         "cpu_baseline": cpu,
         "source_hash": src_hash,
     }

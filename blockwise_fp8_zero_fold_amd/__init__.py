@@ -8,5 +8,5 @@ Importing this package loads the library and raises if it is not built.
 from ._lib import (  # noqa: F401
     ALL_RANKS, BF16, E4M3, F32, SPLIT_BLOCK, SPLIT_PARAM, BLOCK_ENTRY_DTYPE, Fp8z1Error, Hparams, State, Table,
     fp8z1_build_table, fp8z1_encode_e4m3, fp8z1_fold, fp8z1_state_init, fp8z1_state_read, fp8z1_state_write,
-    fp8z1_step, fp8z1_step_workspace_bytes, fp8z1_unfold, lib, lib_path,
+    fp8z1_step, fp8z1_step_rowmajor, fp8z1_step_workspace_bytes, fp8z1_unfold, lib, lib_path,
 )

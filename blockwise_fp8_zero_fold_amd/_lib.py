@@ -88,6 +88,8 @@ _sig = {
     "fp8z1_step_workspace_bytes": (C.c_int, [_vp, C.POINTER(C.c_size_t)]),
     "fp8z1_step": (C.c_int, [_vp, C.POINTER(Hparams), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_size_t, C.c_int32,
                              _vp]),
+    "fp8z1_step_rowmajor": (C.c_int, [_vp, C.POINTER(Hparams), _vp, C.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, _vp,
+                                      C.c_size_t, _vp]),
     "fp8z1_unfold": (C.c_int, [_vp, _vp, C.c_int32, _vp, C.POINTER(_vp), C.POINTER(_vp), _vp]),
     "fp8z1_state_read": (C.c_int, [_vp, C.POINTER(State), _vp]),
     "fp8z1_state_write": (C.c_int, [_vp, C.POINTER(State), _vp]),
@@ -260,6 +262,24 @@ def fp8z1_step(table: Table, hp: Hparams, d_state, grad, master, m, v, fp8, scal
     _check(lib.fp8z1_step(table.handle, C.byref(hp), _ptr(d_state), _ptr(grad), _ptr(master), _ptr(m), _ptr(v),
                           _ptr(fp8), _ptr(scales), _ptr(workspace), workspace_bytes, int(bool(presummed)),
                           _stream(stream)), "fp8z1_step")
+
+
+def fp8z1_step_rowmajor(table: Table, hp: Hparams, d_state, grads: Sequence, master, m, v, fp8, scales,
+                        workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+    if workspace is not None and not workspace_bytes and _is_tensor(workspace):
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    n = table.shard_slots
+    for name, x in (("master", master), ("m", m), ("v", v)):
+        _need(x, n * 16384 * 4, f"step_rowmajor {name}")
+    _need(fp8, n * 16384, "step_rowmajor fp8")
+    _need(scales, n * 4, "step_rowmajor scales")
+    _need(d_state, 64, "step_rowmajor state")
+    if workspace is not None:
+        _need(workspace, n * 8, "step_rowmajor workspace")
+    _check_param_list(table, grads, F32, "step_rowmajor grads")
+    _check(lib.fp8z1_step_rowmajor(table.handle, C.byref(hp), _ptr(d_state), _ptr_list(grads), _ptr(master), _ptr(m),
+                                   _ptr(v), _ptr(fp8), _ptr(scales), _ptr(workspace), workspace_bytes,
+                                   _stream(stream)), "fp8z1_step_rowmajor")
 
 
 def fp8z1_unfold(table: Table, folded, dtype: int, scales, dsts: Sequence, dst_scales: Optional[Sequence] = None,

@@ -39,7 +39,9 @@ struct Src<uint16_t> {  // bfloat16 bits
   __device__ static float load1(const uint16_t* p) { return widen(*p); }
 };
 
-template <typename T, bool SUMSQ>
+// WRITE = false: statistics only (the per-slot sums of a row-major grad that is
+// read by the update directly, without a folded copy).
+template <typename T, bool SUMSQ, bool WRITE = true>
 __global__ __launch_bounds__(kFoldThreads) void fold_kernel(const SlotPlan* __restrict__ plan,
                                                             const void* const* __restrict__ srcs,
                                                             float* __restrict__ dst,
@@ -47,13 +49,15 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(const SlotPlan* __re
   __shared__ double red[kFoldThreads / 64];
   const int64_t s = blockIdx.x;
   const SlotPlan P = plan[s];
-  float4* out = reinterpret_cast<float4*>(dst + s * kBlockElems);
+  float4* out = WRITE ? reinterpret_cast<float4*>(dst + s * kBlockElems) : nullptr;
   const int t = threadIdx.x;
   double acc = 0.0;
 
   if (P.param < 0) {
+    if (WRITE) {
 #pragma unroll
-    for (int k = 0; k < kPasses; ++k) out[t + kFoldThreads * k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < kPasses; ++k) out[t + kFoldThreads * k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   } else {
     const T* src = static_cast<const T*>(srcs[P.param]) + P.off;
     const int64_t ld = P.ld;
@@ -82,7 +86,7 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(const SlotPlan* __re
     }
 #pragma unroll
     for (int k = 0; k < kPasses; ++k) {
-      out[t + kFoldThreads * k] = x[k];
+      if (WRITE) out[t + kFoldThreads * k] = x[k];
       if (SUMSQ) {
         // padding positions hold +0 and add nothing
         acc += sq64(x[k].x);
@@ -111,6 +115,14 @@ hipError_t launch(const SlotPlan* plan, void** srcs, float* dst, double* sumsq, 
 }
 
 }  // namespace
+
+hipError_t launch_grad_sumsq(const SlotPlan* plan, void** grads, double* sumsq, int64_t nslots, hipStream_t stream) {
+  if (nslots == 0) return hipSuccess;
+  hipLaunchKernelGGL((fold_kernel<float, true, false>), dim3(nslots), dim3(kFoldThreads), 0, stream, plan, grads,
+                     nullptr, sumsq);
+  return hipGetLastError();
+}
+
 }  // namespace fp8z1
 
 using namespace fp8z1;

@@ -28,7 +28,7 @@ struct SlotPlan {
 };
 static_assert(sizeof(SlotPlan) == 32, "SlotPlan is 32 bytes");
 
-enum PtrRole { kRoleFoldSrc = 0, kRoleUnfoldDst = 1, kRoleUnfoldScale = 2, kNumRoles = 3 };
+enum PtrRole { kRoleFoldSrc = 0, kRoleUnfoldDst = 1, kRoleUnfoldScale = 2, kRoleStepGrad = 3, kNumRoles = 4 };
 
 // Device-side pointer list for one role: a pinned host mirror, the device
 // array and an event marking the end of the last upload from the mirror.
@@ -62,3 +62,12 @@ int device_ptr_list(fp8z1_table* t, PtrRole role, const void* const* host_list, 
 int check_hip(int hip_status, const char* what);
 
 }  // namespace fp8z1
+
+#ifdef __HIPCC__
+#include <hip/hip_runtime.h>
+namespace fp8z1 {
+// Per-slot float64 sums of squares of row-major FP32 grads (no folded copy),
+// in the same order as the fold's fused statistics.
+hipError_t launch_grad_sumsq(const SlotPlan* plan, void** grads, double* sumsq, int64_t nslots, hipStream_t stream);
+}  // namespace fp8z1
+#endif

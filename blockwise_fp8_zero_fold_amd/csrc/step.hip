@@ -193,9 +193,40 @@ __device__ __forceinline__ uint32_t pack_codes(float4 x, float s) {
          (e4m3_encode(x.w / s) << 24);
 }
 
+// Where the update reads the grads from: the folded shard (the fold ran
+// before), or the row-major params directly (the fold happens on read and no
+// folded copy of the grads is written).
+template <bool ROWMAJOR>
+struct GradSrc {
+  const float4* folded;  // this slot's folded grads (!ROWMAJOR)
+  const float* rows;     // element (0, 0) of this slot's block (ROWMAJOR)
+  int64_t ld;            // row stride (ROWMAJOR)
+  bool vec;              // rows are 16-byte aligned (ROWMAJOR)
+
+  __device__ __forceinline__ float4 chunk(int c) const {
+    if (!ROWMAJOR) return folded[c];
+    return *reinterpret_cast<const float4*>(rows + (c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow));
+  }
+  // elements j .. j+3 of row i, those at columns >= vc read as 0
+  __device__ __forceinline__ void chunk_masked(int c, int i, int j, int vc, float g[4]) const {
+    if (!ROWMAJOR || (vec && j + 4 <= vc)) {
+      const float4 x = ROWMAJOR ? *reinterpret_cast<const float4*>(rows + i * ld + j) : folded[c];
+      g[0] = x.x;
+      g[1] = x.y;
+      g[2] = x.z;
+      g[3] = x.w;
+      return;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] = j + e < vc ? rows[i * ld + j + e] : 0.0f;
+  }
+};
+
+template <bool ROWMAJOR>
 __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __restrict__ plan,
                                                              const fp8z1_state* __restrict__ st,
                                                              const float* __restrict__ grad,
+                                                             void* const* __restrict__ grad_rows,
                                                              float* __restrict__ master, float* __restrict__ mom1,
                                                              float* __restrict__ mom2, uint8_t* __restrict__ fp8,
                                                              float* __restrict__ scales, UpdateArgs a) {
@@ -214,7 +245,18 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
     return;
   }
   const int64_t base = s * (kBlockElems / 4);
-  const float4* g4 = reinterpret_cast<const float4*>(grad) + base;
+  GradSrc<ROWMAJOR> G;
+  if (ROWMAJOR) {
+    G.folded = nullptr;
+    G.rows = static_cast<const float*>(grad_rows[P.param]) + P.off;
+    G.ld = P.ld;
+    G.vec = (P.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(G.rows) % 16) == 0;
+  } else {
+    G.folded = reinterpret_cast<const float4*>(grad) + base;
+    G.rows = nullptr;
+    G.ld = 0;
+    G.vec = true;
+  }
   float4* p4 = reinterpret_cast<float4*>(master) + base;
   float4* m4 = reinterpret_cast<float4*>(mom1) + base;
   float4* v4 = reinterpret_cast<float4*>(mom2) + base;
@@ -222,11 +264,12 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
   float4 pn[kUpdPasses];
   float amax = 0.0f;
   const int vr = P.vr, vc = P.vc;
-  if (vr == kB && vc == kB) {
+  const bool full = vr == kB && vc == kB;
+  if (full && G.vec) {
 #pragma unroll
     for (int q = 0; q < kUpdPasses; ++q) {
       const int c = t + kUpdThreads * q;
-      const float4 g = g4[c], p = p4[c], m = m4[c], v = v4[c];
+      const float4 g = G.chunk(c), p = p4[c], m = m4[c], v = v4[c];
       const Moments e0 = adamw1(g.x, p.x, m.x, v.x, k, decay, step_size, bc2, a);
       const Moments e1 = adamw1(g.y, p.y, m.y, v.y, k, decay, step_size, bc2, a);
       const Moments e2 = adamw1(g.z, p.z, m.z, v.z, k, decay, step_size, bc2, a);
@@ -238,18 +281,19 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e0.p), fabsf(e1.p)), fmaxf(fabsf(e2.p), fabsf(e3.p))));
     }
   } else {
-    // partial block: padding positions are neither used nor changed (their
-    // loaded values are written back as they were); they count 0 in amax
+    // partial block (or rows that are not 16-byte aligned): padding positions
+    // are neither used nor changed (their loaded values are written back as
+    // they were) and count 0 in amax
 #pragma unroll
     for (int q = 0; q < kUpdPasses; ++q) {
       const int c = t + kUpdThreads * q;
       const int i = c / kChunksPerRow, j = 4 * (c % kChunksPerRow);
       pn[q] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (i < vr && j < vc) {
-        const float4 g = g4[c], p = p4[c], m = m4[c], v = v4[c];
-        float4 np = p, nm = m, nv = v;
-        const float gg[4] = {g.x, g.y, g.z, g.w}, pp[4] = {p.x, p.y, p.z, p.w}, mm[4] = {m.x, m.y, m.z, m.w},
-                    vv[4] = {v.x, v.y, v.z, v.w};
+        float gg[4];
+        G.chunk_masked(c, i, j, vc, gg);
+        const float4 p = p4[c], m = m4[c], v = v4[c];
+        const float pp[4] = {p.x, p.y, p.z, p.w}, mm[4] = {m.x, m.y, m.z, m.w}, vv[4] = {v.x, v.y, v.z, v.w};
         float op[4] = {p.x, p.y, p.z, p.w}, om[4] = {m.x, m.y, m.z, m.w}, ov[4] = {v.x, v.y, v.z, v.w};
         float qn[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -263,12 +307,9 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
             amax = fmaxf(amax, fabsf(r.p));
           }
         }
-        np = make_float4(op[0], op[1], op[2], op[3]);
-        nm = make_float4(om[0], om[1], om[2], om[3]);
-        nv = make_float4(ov[0], ov[1], ov[2], ov[3]);
-        p4[c] = np;
-        m4[c] = nm;
-        v4[c] = nv;
+        p4[c] = make_float4(op[0], op[1], op[2], op[3]);
+        m4[c] = make_float4(om[0], om[1], om[2], om[3]);
+        v4[c] = make_float4(ov[0], ov[1], ov[2], ov[3]);
         pn[q] = make_float4(qn[0], qn[1], qn[2], qn[3]);
       }
     }
@@ -276,7 +317,7 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
 
   amax = block_max<kUpdThreads>(amax, red);
   const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
-  if (vr == kB && vc == kB) {
+  if (full) {
 #pragma unroll
     for (int q = 0; q < kUpdPasses; ++q) codes[t + kUpdThreads * q] = pack_codes(pn[q], scale);
   } else {
@@ -325,38 +366,59 @@ extern "C" int fp8z1_step_workspace_bytes(const fp8z1_table* t, size_t* bytes) {
   return FP8Z1_OK;
 }
 
-extern "C" int fp8z1_step(const fp8z1_table* ct, const fp8z1_hparams* hp, fp8z1_state* d_state, const float* grad,
-                          float* master, float* m, float* v, uint8_t* fp8, float* scales, void* d_workspace,
-                          size_t workspace_bytes, int32_t presummed, void* stream) {
-  fp8z1_table* t = const_cast<fp8z1_table*>(ct);
-  if (!t || !hp || !d_state || !grad || !master || !m || !v || !fp8 || !scales)
-    return set_error(FP8Z1_EINVAL, "step: NULL argument");
-  if (!aligned16(grad) || !aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(fp8))
-    return set_error(FP8Z1_EINVAL, "step: grad, master, m, v and fp8 must be 16-byte aligned");
+namespace {
+
+int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, const float* grad,
+              const void* const* grad_rows, float* master, float* m, float* v, uint8_t* fp8, float* scales,
+              void* d_workspace, size_t workspace_bytes, int32_t presummed, void* stream) {
+  const char* who = grad_rows ? "step_rowmajor" : "step";
+  if (!t || !hp || !d_state || !(grad || grad_rows) || !master || !m || !v || !fp8 || !scales)
+    return set_error(FP8Z1_EINVAL, std::string(who) + ": NULL argument");
+  if ((grad && !aligned16(grad)) || !aligned16(master) || !aligned16(m) || !aligned16(v) || !aligned16(fp8))
+    return set_error(FP8Z1_EINVAL, std::string(who) + ": grad, master, m, v and fp8 must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(scales) % 4 || reinterpret_cast<uintptr_t>(d_state) % 8)
-    return set_error(FP8Z1_EINVAL, "step: misaligned scales or state");
+    return set_error(FP8Z1_EINVAL, std::string(who) + ": misaligned scales or state");
   if (!(hp->beta1 >= 0.0f && hp->beta1 < 1.0f && hp->beta2 >= 0.0f && hp->beta2 < 1.0f))
-    return set_error(FP8Z1_EINVAL, "step: betas must be in [0, 1)");
+    return set_error(FP8Z1_EINVAL, std::string(who) + ": betas must be in [0, 1)");
   if (!(hp->eps > 0.0f) || !std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay))
-    return set_error(FP8Z1_EINVAL, "step: eps must be > 0, lr and weight_decay finite");
+    return set_error(FP8Z1_EINVAL, std::string(who) + ": eps must be > 0, lr and weight_decay finite");
   if (hp->loss_scaling && hp->growth_interval < 1)
-    return set_error(FP8Z1_EINVAL, "step: growth_interval must be >= 1");
+    return set_error(FP8Z1_EINVAL, std::string(who) + ": growth_interval must be >= 1");
+  if (grad_rows) {
+    for (const fp8z1_block& e : t->entries) {
+      if (e.param < 0) continue;
+      const void* p = grad_rows[e.param];
+      if (!p || reinterpret_cast<uintptr_t>(p) % 4)
+        return set_error(FP8Z1_EINVAL, std::string(who) + ": grad pointer of param " + std::to_string(e.param) +
+                                           " is NULL or misaligned");
+    }
+  }
   const bool stats = hp->max_grad_norm > 0.0f || hp->loss_scaling != 0;
   const int64_t n = t->info.shard_slots;
   if (stats) {
-    if (!d_workspace) return set_error(FP8Z1_EINVAL, "step: statistics need the workspace");
+    if (!d_workspace) return set_error(FP8Z1_EINVAL, std::string(who) + ": statistics need the workspace");
     if (workspace_bytes < static_cast<size_t>(n) * sizeof(double))
-      return set_error(FP8Z1_EINVAL, "step: workspace smaller than fp8z1_step_workspace_bytes()");
-    if (reinterpret_cast<uintptr_t>(d_workspace) % 8) return set_error(FP8Z1_EINVAL, "step: misaligned workspace");
+      return set_error(FP8Z1_EINVAL, std::string(who) + ": workspace smaller than fp8z1_step_workspace_bytes()");
+    if (reinterpret_cast<uintptr_t>(d_workspace) % 8)
+      return set_error(FP8Z1_EINVAL, std::string(who) + ": misaligned workspace");
   }
   std::lock_guard<std::mutex> lock(t->mu);
   int rc = ensure_device(t);
   if (rc) return rc;
+  void** drows = nullptr;
+  if (grad_rows) {
+    rc = device_ptr_list(t, kRoleStepGrad, grad_rows, &drows, stream);
+    if (rc) return rc;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   double* partial = static_cast<double*>(d_workspace);
   if (stats && !presummed && n > 0) {
-    hipLaunchKernelGGL(sumsq_kernel, dim3(n), dim3(kSumThreads), 0, s, t->d_plan, grad, partial);
-    rc = check_hip(hipGetLastError(), "step: statistics launch");
+    if (grad_rows)
+      rc = check_hip(launch_grad_sumsq(t->d_plan, drows, partial, n, s), "step: statistics launch");
+    else {
+      hipLaunchKernelGGL(sumsq_kernel, dim3(n), dim3(kSumThreads), 0, s, t->d_plan, grad, partial);
+      rc = check_hip(hipGetLastError(), "step: statistics launch");
+    }
     if (rc) return rc;
   }
   FinalizeArgs fa;
@@ -383,9 +445,31 @@ extern "C" int fp8z1_step(const fp8z1_table* ct, const fp8z1_hparams* hp, fp8z1_
   ua.one_minus_beta1 = static_cast<float>(1.0 - static_cast<double>(hp->beta1));
   ua.one_minus_beta2 = static_cast<float>(1.0 - static_cast<double>(hp->beta2));
   ua.eps = hp->eps;
-  hipLaunchKernelGGL(update_kernel, dim3(n), dim3(kUpdThreads), 0, s, t->d_plan, d_state, grad, master, m, v, fp8,
-                     scales, ua);
+  if (grad_rows)
+    hipLaunchKernelGGL(update_kernel<true>, dim3(n), dim3(kUpdThreads), 0, s, t->d_plan, d_state, nullptr, drows,
+                       master, m, v, fp8, scales, ua);
+  else
+    hipLaunchKernelGGL(update_kernel<false>, dim3(n), dim3(kUpdThreads), 0, s, t->d_plan, d_state, grad, nullptr,
+                       master, m, v, fp8, scales, ua);
   return check_hip(hipGetLastError(), "step: update launch");
+}
+
+}  // namespace
+
+extern "C" int fp8z1_step(const fp8z1_table* ct, const fp8z1_hparams* hp, fp8z1_state* d_state, const float* grad,
+                          float* master, float* m, float* v, uint8_t* fp8, float* scales, void* d_workspace,
+                          size_t workspace_bytes, int32_t presummed, void* stream) {
+  if (!grad) return set_error(FP8Z1_EINVAL, "step: NULL argument");
+  return step_impl(const_cast<fp8z1_table*>(ct), hp, d_state, grad, nullptr, master, m, v, fp8, scales, d_workspace,
+                   workspace_bytes, presummed, stream);
+}
+
+extern "C" int fp8z1_step_rowmajor(const fp8z1_table* ct, const fp8z1_hparams* hp, fp8z1_state* d_state,
+                                   const void* const* grads, float* master, float* m, float* v, uint8_t* fp8,
+                                   float* scales, void* d_workspace, size_t workspace_bytes, void* stream) {
+  if (!grads) return set_error(FP8Z1_EINVAL, "step_rowmajor: NULL argument");
+  return step_impl(const_cast<fp8z1_table*>(ct), hp, d_state, nullptr, grads, master, m, v, fp8, scales,
+                   d_workspace, workspace_bytes, 0, stream);
 }
 
 extern "C" int fp8z1_encode_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {

@@ -64,10 +64,20 @@ class Shard:
         L.fp8z1_unfold(self.table, self.fp8, L.E4M3, self.scales if scales is not None else None, codes, scales,
                        stream=stream)
 
-    def step(self, hp: L.Hparams, grads, codes, scales=None, fused_stats: bool = True, stream=None) -> None:
-        """The whole per-step path: fold grads -> update + requant -> unfold."""
-        pre = self.fold_grads(hp, grads, fused_stats=fused_stats, stream=stream)
-        self.update(hp, presummed=pre, stream=stream)
+    def update_rowmajor(self, hp: L.Hparams, grads: Sequence[Optional[torch.Tensor]], stream=None) -> None:
+        """Update + requant reading the row-major grads directly (fold on read)."""
+        L.fp8z1_step_rowmajor(self.table, hp, self.state, grads, self.master, self.m, self.v, self.fp8, self.scales,
+                              workspace=self.workspace, stream=stream)
+
+    def step(self, hp: L.Hparams, grads, codes, scales=None, fused_stats: bool = True, fold_on_read: bool = False,
+             stream=None) -> None:
+        """The whole per-step path: fold grads -> update + requant -> unfold (or, with
+        fold_on_read, update + requant reading the row-major grads -> unfold)."""
+        if fold_on_read:
+            self.update_rowmajor(hp, grads, stream=stream)
+        else:
+            pre = self.fold_grads(hp, grads, fused_stats=fused_stats, stream=stream)
+            self.update(hp, presummed=pre, stream=stream)
         self.unfold(codes, scales, stream=stream)
 
     def read_state(self, stream=None) -> dict:

@@ -195,6 +195,19 @@ int fp8z1_step(const fp8z1_table* table, const fp8z1_hparams* hp, fp8z1_state* d
                float* master, float* m, float* v, uint8_t* fp8, float* scales, void* d_workspace,
                size_t workspace_bytes, int32_t presummed, void* stream);
 
+/* The same step with the grads read straight from the row-major reduced
+ * grads: the fold of section "参数布局变换" happens on read inside the
+ * update, and no folded copy of the grads is written.  grads: host array of
+ * n_params device pointers to row-major FP32 [E,R,C] grads, 4-byte aligned
+ * (NULL allowed for params the shard holds no block of).  With statistics
+ * on, a first pass over the same grads writes the per-slot sums of squares
+ * into d_workspace, in the order fp8z1_fold uses.  Results (state, master,
+ * m, v, fp8, scales) are bit-identical to fp8z1_fold followed by
+ * fp8z1_step. */
+int fp8z1_step_rowmajor(const fp8z1_table* table, const fp8z1_hparams* hp, fp8z1_state* d_state,
+                        const void* const* grads, float* master, float* m, float* v, uint8_t* fp8, float* scales,
+                        void* d_workspace, size_t workspace_bytes, void* stream);
+
 /* Unfold (section "参数布局变换", and the scale unfold of section "总结"):
  * write the shard's real elements from `folded` (device, shard_slots*16384
  * elements of dtype FP8Z1_E4M3 or FP8Z1_F32) into row-major params.

@@ -1,5 +1,5 @@
-"""GPU parity at the full workload sizes, in the launch configuration bench.py times
-(fold with fused statistics when statistics are on, then step, then unfold):
+"""GPU parity at the full workload sizes, in the launch configurations bench.py times
+(update reading the row-major grads, or fold with fused statistics then update; then unfold):
 sampled slots are checked bit for bit against the oracle, which recomputes them
 one by one from the same seeded inputs; properties that hold at any size are
 checked on every slot."""
@@ -65,7 +65,8 @@ def _slab_sumsq(ent, slab, p, e):
 
 
 @pytest.mark.parametrize("name,steps", [("moe", 5), ("dense", 3), ("full", 4), ("ragged", 2)])
-def test_full_size_sampled(name, steps):
+@pytest.mark.parametrize("fold_on_read", [True, False])
+def test_full_size_sampled(name, steps, fold_on_read):
     fz = _fz()
     from blockwise_fp8_zero_fold_amd.shard import Shard
     from tests import gpu_harness as gh
@@ -137,7 +138,7 @@ def test_full_size_sampled(name, steps):
         else:
             hp = fz.Hparams.make(w.hp)
         del G
-        sh.step(hp, grads, dst_codes, dst_scales, fused_stats=True)
+        sh.step(hp, grads, dst_codes, dst_scales, fused_stats=True, fold_on_read=fold_on_read)
         del grads
         st, master, m, v, codes, sc = ostep.step_sharded(sub, w.hp, st, g_sub, master, m, v, codes, sc,
                                                          extra_sumsq=extra)

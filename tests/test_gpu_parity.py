@@ -160,7 +160,7 @@ def _codes_bar(got, want, what):
     assert (d > 0).mean() <= 1e-4, f"{what}: {(d > 0).mean()} of codes differ by 1 ulp"
 
 
-def _run_parity(w, ranks=None, fused=None):
+def _run_parity(w, ranks=None, fused=None, fold_on_read=False):
     gh = _gh()
     from blockwise_fp8_zero_fold_amd.shard import Shard
     ranks = w.ranks if ranks is None else ranks
@@ -188,10 +188,11 @@ def _run_parity(w, ranks=None, fused=None):
             R = ref[r][t - 1]
             hp = fz.Hparams.make(w.hp, extra_sumsq=R["extra"])
             use_fused = (t % 2 == 0) if fused is None else fused
-            sh.step(hp, gh.grad_tensors(w, held, t), codes, scales, fused_stats=use_fused)
+            sh.step(hp, gh.grad_tensors(w, held, t), codes, scales, fused_stats=use_fused, fold_on_read=fold_on_read)
             torch.cuda.synchronize()
-            tag = f"{w.name} rank {r} step {t}"
-            assert gh.bits_equal(gh.folded(sh.grad, n), R["grad"]), f"{tag}: grad fold"
+            tag = f"{w.name} rank {r} step {t}" + (" (fold on read)" if fold_on_read else "")
+            if not fold_on_read:
+                assert gh.bits_equal(gh.folded(sh.grad, n), R["grad"]), f"{tag}: grad fold"
             st = sh.read_state()
             want_st = R["state"]
             for key in ("step", "found_inf", "skipped_total", "good_steps"):
@@ -223,14 +224,16 @@ def _run_parity(w, ranks=None, fused=None):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_clip", "tiny_lossscale", "dense_small", "moe_small", "full_small"])
-def test_step_parity(name):
-    _run_parity(synth.get(name))
+@pytest.mark.parametrize("fold_on_read", [False, True])
+def test_step_parity(name, fold_on_read):
+    _run_parity(synth.get(name), fold_on_read=fold_on_read)
 
 
 @pytest.mark.parametrize("split", ["block", "param"])
-def test_step_parity_ragged(split):
+@pytest.mark.parametrize("fold_on_read", [False, True])
+def test_step_parity_ragged(split, fold_on_read):
     w = synth.get("ragged_small").with_(split=split)
-    _run_parity(w, ranks=[0, 5, 7, 15])
+    _run_parity(w, ranks=[0, 5, 7, 15], fold_on_read=fold_on_read)
 
 
 def test_padding_poison_gpu():
@@ -311,3 +314,4 @@ def test_empty_and_degenerate_blocks():
     w = synth.Workload(name="degen", shapes=((1, 1, 1), (1, 129, 1), (2, 1, 130)), dp=3, ranks=(0, 1, 2), steps=2,
                        hp=synth.Hparams(max_grad_norm=1.0), grad_sigma=0.0, master_sigma=0.0)
     _run_parity(w)
+    _run_parity(w, fold_on_read=True)

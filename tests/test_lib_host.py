@@ -115,6 +115,12 @@ def test_argument_errors_before_any_gpu_work():
     hp_bad = fz.Hparams.make(synth.Hparams(beta1=1.0))
     with pytest.raises(fz.Fp8z1Error, match="betas"):
         fz.fp8z1_step(t, hp_bad, 16, 16, 16, 16, 16, 16, 16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="NULL or misaligned"):
+        fz.fp8z1_step_rowmajor(t, hp, 16, [None], 16, 16, 16, 16, 16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="NULL or misaligned"):
+        fz.fp8z1_step_rowmajor(t, hp, 16, [18], 16, 16, 16, 16, 16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="workspace"):
+        fz.fp8z1_step_rowmajor(t, hp_clip, 16, [16], 16, 16, 16, 16, 16, stream=0)
     with pytest.raises(fz.Fp8z1Error, match="dtype"):
         fz.fp8z1_unfold(t, 16, fz.BF16, None, [16], stream=0)
     with pytest.raises(fz.Fp8z1Error, match="NULL"):
