@@ -152,6 +152,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="moe", choices=["moe", "dense", "full", "ragged"])
+    ap.add_argument("--split", default=None, choices=["block", "param"], help="override the workload's split")
     ap.add_argument("--mode", default="fold_on_read", choices=["fold_on_read", "fold"],
                     help="headline route: the update reads the row-major grads (fold on read), or a separate "
                          "fold kernel writes folded grads first; the other route is timed too and reported "
@@ -185,6 +186,8 @@ def main() -> int:
     from blockwise_fp8_zero_fold_amd.shard import Shard
 
     w = synth.get(args.workload)
+    if args.split:
+        w = w.with_(split=args.split)
     rank = w.ranks[0]
     split = fz.SPLIT_PARAM if w.split == "param" else fz.SPLIT_BLOCK
     torch.cuda.set_device(0)

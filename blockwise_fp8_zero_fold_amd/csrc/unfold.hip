@@ -3,12 +3,14 @@
 // 优化器设计", section "参数布局变换" and the parameter/scale unfold of section
 // "总结").  Only real positions are written: padding is dropped.
 //
-// As in the fold, whole row segments move (no element transpose).  One
-// workgroup per slot.  FP8 codes: a 128-byte row segment is 8 lanes of
-// 16-byte stores when the destination rows are 16-byte aligned and the
-// block has all 128 columns; otherwise single-byte stores, which never touch
-// a byte that belongs to a neighbouring block.  float32 (used for round-trip
-// checks): the same with 16-byte / 4-byte accesses.
+// As in the fold, whole row segments move (no element transpose).  FP8
+// codes: four workgroups per slot, each a quarter of the block; a 128-byte row
+// segment is 8 lanes of 16-byte stores when the destination rows are 16-byte
+// aligned and the block has all 128 columns; otherwise the rows are staged in
+// LDS and written with aligned 4-byte stores plus single bytes at the row
+// ends, which never touch a byte that belongs to a neighbouring block.
+// float32 (used for round-trip checks): one workgroup per slot, 16-byte or
+// 4-byte stores.
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"
@@ -18,38 +20,61 @@ namespace {
 
 constexpr int kUnfThreads = 256;
 
+// FP8 codes: a workgroup moves a quarter of a block (32 rows x 128 bytes,
+// 4 KB), so that the workgroups in flight cover a compact range of memory.
+constexpr int kUnfRows = 32;
+constexpr int kUnfParts = kB / kUnfRows;
+constexpr int kUnfWordsPerRow = (3 + kB + 3) / 4;  // 4-byte words touched by a 128-byte row at any alignment
+
 __global__ __launch_bounds__(kUnfThreads) void unfold_e4m3_kernel(const SlotPlan* __restrict__ plan,
                                                                   const uint8_t* __restrict__ folded,
                                                                   void* const* __restrict__ dsts,
                                                                   const float* __restrict__ scales,
                                                                   float* const* __restrict__ dscales) {
-  const int64_t s = blockIdx.x;
+  __shared__ uint32_t stage[kUnfRows * kB / 4 + 4];  // the part's rows, plus one word of slack per row end
+  const int64_t s = blockIdx.x / kUnfParts;
+  const int part = blockIdx.x % kUnfParts;
   const SlotPlan P = plan[s];
   if (P.param < 0) return;
   const int t = threadIdx.x;
-  if (dscales && t == 0) dscales[P.param][P.soff] = scales[s];
-  uint8_t* dst = static_cast<uint8_t*>(dsts[P.param]) + P.off;
-  const uint8_t* src = folded + s * kBlockElems;
-  const int64_t ld = P.ld;
+  if (dscales && part == 0 && t == 0) dscales[P.param][P.soff] = scales[s];
   const int vr = P.vr, vc = P.vc;
+  const int r0 = part * kUnfRows;
+  if (r0 >= vr) return;
+  const int nrows = min(kUnfRows, vr - r0);
+  const int64_t ld = P.ld;
+  uint8_t* dst = static_cast<uint8_t*>(dsts[P.param]) + P.off + r0 * ld;
+  const uint4* src = reinterpret_cast<const uint4*>(folded + s * kBlockElems + r0 * kB);
   if (vc == kB && (ld % 16) == 0 && (reinterpret_cast<uintptr_t>(dst) % 16) == 0) {
-    // 8 lanes per 128-byte row, 32 rows per pass
-    const uint4* s4 = reinterpret_cast<const uint4*>(src);
-    uint4 x[kB / 32];
+    // 8 lanes per 128-byte row, one 16-byte load and store per lane
+    const int i = t >> 3;
+    if (i < nrows) *reinterpret_cast<uint4*>(dst + i * ld + 16 * (t & 7)) = src[t];
+    return;
+  }
+  // Rows that are not 16-byte aligned, or shorter than 128 bytes: stage the rows
+  // in LDS, then write each destination row with aligned 4-byte stores inside
+  // the row and single bytes in the (at most two) words it shares with the
+  // neighbouring blocks, so no byte outside the row is written.
+  if (t < nrows * (kB / 16)) reinterpret_cast<uint4*>(stage)[t] = src[t];
+  if (t < 4) stage[kUnfRows * kB / 4 + t] = 0u;
+  __syncthreads();
+  const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
+  for (int f = t; f < nrows * kUnfWordsPerRow; f += kUnfThreads) {
+    const int i = f / kUnfWordsPerRow, w = f % kUnfWordsPerRow;
+    uint8_t* row = dst + i * ld;
+    const int head = static_cast<int>(reinterpret_cast<uintptr_t>(row) & 3u);
+    const int o = 4 * w - head;  // row offset of this word's first byte; row + o is 4-byte aligned
+    if (o >= vc) continue;
+    if (o >= 0 && o + 4 <= vc) {
+      const uint32_t lo = stage[i * (kB / 4) + (o >> 2)];
+      const uint32_t hi = stage[i * (kB / 4) + (o >> 2) + 1];
+      *reinterpret_cast<uint32_t*>(row + o) = __builtin_amdgcn_alignbyte(hi, lo, static_cast<uint32_t>(o & 3));
+    } else {
 #pragma unroll
-    for (int q = 0; q < kB / 32; ++q) {
-      const int i = (t >> 3) + 32 * q;
-      if (i < vr) x[q] = s4[i * 8 + (t & 7)];
-    }
-#pragma unroll
-    for (int q = 0; q < kB / 32; ++q) {
-      const int i = (t >> 3) + 32 * q;
-      if (i < vr) *reinterpret_cast<uint4*>(dst + i * ld + 16 * (t & 7)) = x[q];
-    }
-  } else {
-    for (int idx = t; idx < kBlockElems; idx += kUnfThreads) {
-      const int i = idx >> 7, j = idx & 127;
-      if (i < vr && j < vc) dst[i * ld + j] = src[idx];
+      for (int b = 0; b < 4; ++b) {
+        const int ob = o + b;
+        if (ob >= 0 && ob < vc) row[ob] = sb[i * kB + ob];
+      }
     }
   }
 }
@@ -122,7 +147,7 @@ extern "C" int fp8z1_unfold(const fp8z1_table* ct, const void* folded, int32_t d
   if (n == 0) return FP8Z1_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == FP8Z1_E4M3)
-    hipLaunchKernelGGL(unfold_e4m3_kernel, dim3(n), dim3(kUnfThreads), 0, s, t->d_plan,
+    hipLaunchKernelGGL(unfold_e4m3_kernel, dim3(n * kUnfParts), dim3(kUnfThreads), 0, s, t->d_plan,
                        static_cast<const uint8_t*>(folded), ddst, with_scales ? scales : nullptr,
                        reinterpret_cast<float* const*>(dsc));
   else
