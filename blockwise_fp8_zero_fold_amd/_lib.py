@@ -30,7 +30,7 @@ class Fp8z1Error(RuntimeError):
 
 
 if not os.path.exists(lib_path):
-    raise ImportError(f"{lib_path} is not built: run `python -m blockwise_fp8_zero_fold_amd.build`")
+    raise ImportError(f"{lib_path} is not built: run `python blockwise_fp8_zero_fold_amd/build.py`")
 lib = C.CDLL(lib_path)
 
 

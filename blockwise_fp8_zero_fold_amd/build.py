@@ -1,6 +1,9 @@
 """Build libfp8z1.so (HIP kernels for gfx950 + host C++) in-tree.
 
-    python -m blockwise_fp8_zero_fold_amd.build
+    python blockwise_fp8_zero_fold_amd/build.py
+
+(run as a script: importing the package loads the library, which a fresh
+checkout does not have yet).
 
 Objects go to <repo>/_build/, the library next to this file.  Every call
 compiles from scratch.

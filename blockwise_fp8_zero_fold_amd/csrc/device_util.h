@@ -68,6 +68,31 @@ __device__ __forceinline__ double block_sum(double v, double* lds) {
   return r;
 }
 
+// Streaming (non-temporal) 16-byte and 4-byte accesses for data that is
+// touched once per kernel: the loads and stores carry the non-temporal hint,
+// so they do not displace other lines in the caches and the stores do not
+// linger as dirty lines.
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+  const v4f_t r = __builtin_nontemporal_load(reinterpret_cast<const v4f_t*>(p));
+  return make_float4(r.x, r.y, r.z, r.w);
+}
+__device__ __forceinline__ void st_stream(float4* p, float4 x) {
+  const v4f_t r = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(r, reinterpret_cast<v4f_t*>(p));
+}
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  const v4u_t r = __builtin_nontemporal_load(reinterpret_cast<const v4u_t*>(p));
+  return make_uint4(r.x, r.y, r.z, r.w);
+}
+__device__ __forceinline__ void st_stream(uint4* p, uint4 x) {
+  const v4u_t r = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(r, reinterpret_cast<v4u_t*>(p));
+}
+__device__ __forceinline__ void st_stream(uint32_t* p, uint32_t x) { __builtin_nontemporal_store(x, p); }
+
 // Square of a float32 value in float64 (exact: a 24-bit significand squared fits in 53 bits).
 __device__ __forceinline__ double sq64(float x) {
   const double d = static_cast<double>(x);

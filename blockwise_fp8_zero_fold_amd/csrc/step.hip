@@ -16,7 +16,7 @@
 //                     unscale factor k, bias-correction scalars, loss scale;
 //                     written to the device state                (level 2)
 //   K3 update_kernel  one workgroup per slot: AdamW on g, p, m, v (16-byte
-//                     loads and stores), the updated block kept in
+//                     streaming loads and stores), the updated block kept in
 //                     registers, block amax (wave shuffles + LDS), scale,
 //                     E4M3 codes.  Returns at once when K2 flagged a skip.
 // K1 is left out when no statistics are needed, or when the fold already
@@ -204,8 +204,8 @@ struct GradSrc {
   bool vec;              // rows are 16-byte aligned (ROWMAJOR)
 
   __device__ __forceinline__ float4 chunk(int c) const {
-    if (!ROWMAJOR) return folded[c];
-    return *reinterpret_cast<const float4*>(rows + (c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow));
+    if (!ROWMAJOR) return ld_stream(folded + c);
+    return ld_stream(reinterpret_cast<const float4*>(rows + (c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow)));
   }
   // elements j .. j+3 of row i, those at columns >= vc read as 0
   __device__ __forceinline__ void chunk_masked(int c, int i, int j, int vc, float g[4]) const {
@@ -269,15 +269,15 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
 #pragma unroll
     for (int q = 0; q < kUpdPasses; ++q) {
       const int c = t + kUpdThreads * q;
-      const float4 g = G.chunk(c), p = p4[c], m = m4[c], v = v4[c];
+      const float4 g = G.chunk(c), p = ld_stream(p4 + c), m = ld_stream(m4 + c), v = ld_stream(v4 + c);
       const Moments e0 = adamw1(g.x, p.x, m.x, v.x, k, decay, step_size, bc2, a);
       const Moments e1 = adamw1(g.y, p.y, m.y, v.y, k, decay, step_size, bc2, a);
       const Moments e2 = adamw1(g.z, p.z, m.z, v.z, k, decay, step_size, bc2, a);
       const Moments e3 = adamw1(g.w, p.w, m.w, v.w, k, decay, step_size, bc2, a);
       pn[q] = make_float4(e0.p, e1.p, e2.p, e3.p);
-      p4[c] = pn[q];
-      m4[c] = make_float4(e0.m, e1.m, e2.m, e3.m);
-      v4[c] = make_float4(e0.v, e1.v, e2.v, e3.v);
+      st_stream(p4 + c, pn[q]);
+      st_stream(m4 + c, make_float4(e0.m, e1.m, e2.m, e3.m));
+      st_stream(v4 + c, make_float4(e0.v, e1.v, e2.v, e3.v));
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e0.p), fabsf(e1.p)), fmaxf(fabsf(e2.p), fabsf(e3.p))));
     }
   } else {
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
   const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
   if (full) {
 #pragma unroll
-    for (int q = 0; q < kUpdPasses; ++q) codes[t + kUpdThreads * q] = pack_codes(pn[q], scale);
+    for (int q = 0; q < kUpdPasses; ++q) st_stream(codes + t + kUpdThreads * q, pack_codes(pn[q], scale));
   } else {
 #pragma unroll
     for (int q = 0; q < kUpdPasses; ++q) {

@@ -5,7 +5,7 @@
 //
 // As in the fold, whole row segments move (no element transpose).  FP8
 // codes: four workgroups per slot, each a quarter of the block; a 128-byte row
-// segment is 8 lanes of 16-byte stores when the destination rows are 16-byte
+// segment is 8 lanes of 16-byte streaming stores when the destination rows are 16-byte
 // aligned and the block has all 128 columns; otherwise the rows are staged in
 // LDS and written with aligned 4-byte stores plus single bytes at the row
 // ends, which never touch a byte that belongs to a neighbouring block.
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kUnfThreads) void unfold_e4m3_kernel(const SlotPlan
   if (vc == kB && (ld % 16) == 0 && (reinterpret_cast<uintptr_t>(dst) % 16) == 0) {
     // 8 lanes per 128-byte row, one 16-byte load and store per lane
     const int i = t >> 3;
-    if (i < nrows) *reinterpret_cast<uint4*>(dst + i * ld + 16 * (t & 7)) = src[t];
+    if (i < nrows) st_stream(reinterpret_cast<uint4*>(dst + i * ld + 16 * (t & 7)), ld_stream(src + t));
     return;
   }
   // Rows that are not 16-byte aligned, or shorter than 128 bytes: stage the rows
