@@ -278,6 +278,34 @@ def main() -> int:
     alt_ms, alt_calls = results[alt_mode]
     alt_total, _ = step_bytes(alt_mode)
 
+    # streaming references measured in the same run: the update's access pattern
+    # with no arithmetic (same slots, same bytes), and a plain 4 KB-per-workgroup copy
+    def ev_time(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3
+
+    probe_bufs = [torch.zeros(nslots * BLOCK, dtype=torch.float32, device="cuda") for _ in range(4)]
+    probe_codes = torch.zeros(nslots * BLOCK, dtype=torch.uint8, device="cuda")
+    t_pat = ev_time(lambda: fz.fp8z1_probe_update_pattern(*probe_bufs, probe_codes, nslots), 10)
+    pat_bytes = 29 * nslots * BLOCK
+    t_copy = ev_time(lambda: fz.fp8z1_probe_copy(probe_bufs[0], probe_bufs[1]), 10)
+    copy_bytes = 2 * probe_bufs[0].numel() * 4
+    del probe_bufs, probe_codes
+    torch.cuda.empty_cache()
+    ceiling = {"update_pattern_gbs": pat_bytes / t_pat / 1e9, "copy_gbs": copy_bytes / t_copy / 1e9,
+               "update_vs_pattern": achieved / (pat_bytes / t_pat / 1e9),
+               "note": "same-run streaming references: fp8z1_probe_update_pattern (the update's loads and stores, "
+                       "no arithmetic, same slot count) and fp8z1_probe_copy (plain copy, 4 KB per workgroup)"}
+    print(f"# ceilings: update pattern {ceiling['update_pattern_gbs']:.0f} GB/s, copy {ceiling['copy_gbs']:.0f} GB/s",
+          file=sys.stderr, flush=True)
+
     cpu = None
     if not args.no_cpu_baseline:
         slots = min(args.cpu_slots, nslots)
@@ -326,6 +354,7 @@ def main() -> int:
             "traffic": _traffic(w.name, args.mode, src_hash),
             "bytes_per_launch": call_bytes,
         },
+        "ceiling": ceiling,
         "alt_mode": {"mode": alt_mode, "ms_per_step": alt_ms, "value": valid / (alt_ms * 1e-3),
                      "per_call_ms": alt_calls, "gbs_algorithmic": alt_total / (alt_ms * 1e-3) / 1e9},
         "cpu_baseline": cpu,

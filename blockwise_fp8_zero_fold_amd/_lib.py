@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libfp8z1.so")
 
 F32, BF16, E4M3 = 0, 1, 2
+SCALE_AMAX, SCALE_POW2 = 0, 1
 SPLIT_BLOCK, SPLIT_PARAM = 0, 1
 ALL_RANKS = -1
 
@@ -53,14 +54,15 @@ class Hparams(C.Structure):
     _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
                 ("weight_decay", C.c_float), ("max_grad_norm", C.c_float), ("loss_scaling", C.c_int32),
                 ("init_scale", C.c_float), ("growth_factor", C.c_float), ("backoff_factor", C.c_float),
-                ("growth_interval", C.c_int32), ("extra_found_inf", C.c_int32), ("extra_sumsq", C.c_double)]
+                ("growth_interval", C.c_int32), ("extra_found_inf", C.c_int32), ("scale_rule", C.c_int32),
+                ("extra_sumsq", C.c_double)]
 
     @classmethod
     def make(cls, hp, extra_sumsq: float = 0.0, extra_found_inf: bool = False) -> "Hparams":
         """From any object with the same attribute names (e.g. synth.Hparams)."""
         return cls(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.max_grad_norm, int(bool(hp.loss_scaling)),
                    hp.init_scale, hp.growth_factor, hp.backoff_factor, int(hp.growth_interval),
-                   int(bool(extra_found_inf)), float(extra_sumsq))
+                   int(bool(extra_found_inf)), int(getattr(hp, "scale_rule", 0)), float(extra_sumsq))
 
 
 class State(C.Structure):
@@ -73,7 +75,7 @@ class State(C.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
-assert C.sizeof(Block) == 16 and C.sizeof(State) == 64
+assert C.sizeof(Block) == 16 and C.sizeof(State) == 64 and C.sizeof(Hparams) == 64
 
 _vp = C.c_void_p
 _sig = {
@@ -94,6 +96,9 @@ _sig = {
     "fp8z1_state_read": (C.c_int, [_vp, C.POINTER(State), _vp]),
     "fp8z1_state_write": (C.c_int, [_vp, C.POINTER(State), _vp]),
     "fp8z1_encode_e4m3": (C.c_int, [_vp, _vp, C.c_int64, _vp]),
+    "fp8z1_dequantize": (C.c_int, [_vp, _vp, C.c_int64, C.c_int64, C.c_int64, C.c_int32, _vp, _vp]),
+    "fp8z1_probe_copy": (C.c_int, [_vp, _vp, C.c_int64, _vp]),
+    "fp8z1_probe_update_pattern": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int64, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(lib, _name)
@@ -312,3 +317,28 @@ def fp8z1_encode_e4m3(x, out, stream=None) -> None:
     _need(x, x.numel() * 4, "encode input", torch.float32)
     _need(out, x.numel(), "encode output", torch.uint8)
     _check(lib.fp8z1_encode_e4m3(_ptr(x), _ptr(out), x.numel(), _stream(stream)), "fp8z1_encode_e4m3")
+
+
+def fp8z1_dequantize(codes, scales, shape, out_dtype: int, out, stream=None) -> None:
+    import torch
+    e, r, c = (int(x) for x in shape)
+    _need(codes, e * r * c, "dequantize codes", torch.uint8)
+    _need(scales, e * (-(-r // 128)) * (-(-c // 128)) * 4, "dequantize scales", torch.float32)
+    _need(out, e * r * c * (4 if out_dtype == F32 else 2), "dequantize out",
+          torch.float32 if out_dtype == F32 else torch.bfloat16)
+    _check(lib.fp8z1_dequantize(_ptr(codes), _ptr(scales), e, r, c, out_dtype, _ptr(out), _stream(stream)),
+           "fp8z1_dequantize")
+
+
+def fp8z1_probe_copy(src, dst, stream=None) -> None:
+    n = src.numel() * src.element_size()
+    _need(dst, n, "probe_copy dst")
+    _check(lib.fp8z1_probe_copy(_ptr(src), _ptr(dst), n, _stream(stream)), "fp8z1_probe_copy")
+
+
+def fp8z1_probe_update_pattern(g, p, m, v, codes, nslots: int, stream=None) -> None:
+    for name, x in (("g", g), ("p", p), ("m", m), ("v", v)):
+        _need(x, nslots * 16384 * 4, f"probe_update_pattern {name}")
+    _need(codes, nslots * 16384, "probe_update_pattern codes")
+    _check(lib.fp8z1_probe_update_pattern(_ptr(g), _ptr(p), _ptr(m), _ptr(v), _ptr(codes), nslots, _stream(stream)),
+           "fp8z1_probe_update_pattern")

@@ -165,9 +165,27 @@ __global__ void state_init_kernel(fp8z1_state* st, float loss_scale) {
 
 struct UpdateArgs {
   float beta1, beta2, one_minus_beta1, one_minus_beta2, eps;
+  int32_t pow2_scale;
 };
 
-constexpr int kUpdThreads = 256;
+// Block scale from the block's amax.  Default: amax / 448 (the largest E4M3
+// value), 1 for an all-zero block.  Power-of-two rule (the E8M0 shared scale of
+// the OCP microscaling formats): 2^(floor(log2 amax) - 8), 8 being the
+// exponent of the largest E4M3 binade, clamped to the E8M0 range from 2^-127.
+__device__ __forceinline__ float block_scale(float amax, bool pow2) {
+  if (!(amax > 0.0f)) return 1.0f;
+  if (!pow2) return amax / 448.0f;
+  const uint32_t u = __float_as_uint(amax);
+  if (u >= 0x7f800000u) return amax;  // +inf
+  const uint32_t ef = u >> 23;
+  // floor(log2 amax): the exponent field for normals; from the leading bit of the
+  // mantissa for subnormals (value = m * 2^-149)
+  const int k = ef ? static_cast<int>(ef) - 127 : (31 - __clz(static_cast<int>(u & 0x7fffffu))) - 149;
+  const int x = max(k - 8, -127);
+  return x >= -126 ? __uint_as_float(static_cast<uint32_t>(x + 127) << 23) : __uint_as_float(1u << (x + 149));
+}
+
+constexpr int kUpdThreads = 512;
 constexpr int kUpdPasses = kChunks / kUpdThreads;
 
 struct Moments {
@@ -316,7 +334,7 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
   }
 
   amax = block_max<kUpdThreads>(amax, red);
-  const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+  const float scale = block_scale(amax, a.pow2_scale != 0);
   if (full) {
 #pragma unroll
     for (int q = 0; q < kUpdPasses; ++q) st_stream(codes + t + kUpdThreads * q, pack_codes(pn[q], scale));
@@ -384,6 +402,8 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
     return set_error(FP8Z1_EINVAL, std::string(who) + ": eps must be > 0, lr and weight_decay finite");
   if (hp->loss_scaling && hp->growth_interval < 1)
     return set_error(FP8Z1_EINVAL, std::string(who) + ": growth_interval must be >= 1");
+  if (hp->scale_rule != FP8Z1_SCALE_AMAX && hp->scale_rule != FP8Z1_SCALE_POW2)
+    return set_error(FP8Z1_EINVAL, std::string(who) + ": scale_rule must be FP8Z1_SCALE_AMAX or FP8Z1_SCALE_POW2");
   if (grad_rows) {
     for (const fp8z1_block& e : t->entries) {
       if (e.param < 0) continue;
@@ -445,6 +465,7 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
   ua.one_minus_beta1 = static_cast<float>(1.0 - static_cast<double>(hp->beta1));
   ua.one_minus_beta2 = static_cast<float>(1.0 - static_cast<double>(hp->beta2));
   ua.eps = hp->eps;
+  ua.pow2_scale = hp->scale_rule == FP8Z1_SCALE_POW2 ? 1 : 0;
   if (grad_rows)
     hipLaunchKernelGGL(update_kernel<true>, dim3(n), dim3(kUpdThreads), 0, s, t->d_plan, d_state, nullptr, drows,
                        master, m, v, fp8, scales, ua);

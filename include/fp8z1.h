@@ -67,6 +67,12 @@ extern "C" {
 
 #define FP8Z1_BLOCK 128 /* block edge */
 
+/* block scale rules */
+#define FP8Z1_SCALE_AMAX 0 /* scale = amax / 448 in float32 (1 if amax = 0) */
+#define FP8Z1_SCALE_POW2 1 /* scale = 2^(floor(log2 amax) - 8), an E8M0 power of two kept in
+                              [2^-127, 2^119] (1 if amax = 0, +inf if amax = +inf); the block's
+                              largest magnitude lands in [256, 512) and saturates at 448 */
+
 typedef struct fp8z1_table fp8z1_table; /* opaque */
 
 typedef struct {
@@ -107,6 +113,7 @@ typedef struct {
   float backoff_factor;    /* S *= backoff_factor on overflow */
   int32_t growth_interval;
   int32_t extra_found_inf; /* overflow flag of the other ranks (the all-reduced flag) */
+  int32_t scale_rule;      /* FP8Z1_SCALE_AMAX (0) or FP8Z1_SCALE_POW2 (1) */
   double extra_sumsq;      /* sum of squares of the other ranks' grads (the all-reduced sum) */
 } fp8z1_hparams;
 
@@ -187,8 +194,9 @@ int fp8z1_step_workspace_bytes(const fp8z1_table* table, size_t* bytes);
  *     Padding positions of master, m, v are neither read for the result nor
  *     changed.
  *  4. per slot: amax = max |p| over real elements, scale = amax/448 (1 if
- *     amax = 0), code = E4M3(p / scale) (round to nearest even, saturating
- *     at 448, NaN kept); padding codes 0; padding slots scale 1.
+ *     amax = 0; or the power of two of FP8Z1_SCALE_POW2 when hp->scale_rule
+ *     asks for it), code = E4M3(p / scale) (round to nearest even,
+ *     saturating at 448, NaN kept); padding codes 0; padding slots scale 1.
  * d_workspace: fp8z1_step_workspace_bytes() bytes (may be NULL when no
  * statistics are taken).  The state at d_state is updated in place. */
 int fp8z1_step(const fp8z1_table* table, const fp8z1_hparams* hp, fp8z1_state* d_state, const float* grad,
@@ -218,6 +226,17 @@ int fp8z1_step_rowmajor(const fp8z1_table* table, const fp8z1_hparams* hp, fp8z1
  * are both non-NULL, each slot's scale goes to its block's position. */
 int fp8z1_unfold(const fp8z1_table* table, const void* folded, int32_t dtype, const float* scales,
                  void* const* dst, float* const* dst_scales, void* stream);
+
+/* Dequantize row-major FP8 weights (section "Blockwise 量化": one scale per
+ * 128x128 block, the scale being the dequantization multiplier):
+ * out[e,r,c] = decode(codes[e,r,c]) * scales[e, r/128, c/128], rounded once to
+ * float32 and, for out_dtype FP8Z1_BF16, then to bfloat16 (nearest, ties to
+ * even; NaN stays NaN).  codes: device [E,R,C] bytes; scales: device
+ * [E,ceil(R/128),ceil(C/128)] float32; out: device [E,R,C] of out_dtype
+ * (FP8Z1_F32 or FP8Z1_BF16).  For reading back what the gathered FP8 weights
+ * stand for. */
+int fp8z1_dequantize(const uint8_t* codes, const float* scales, int64_t E, int64_t R, int64_t C, int32_t out_dtype,
+                     void* out, void* stream);
 
 /* Copy the device state to the host (synchronizes the stream) / from the host
  * (resume from a checkpoint). */

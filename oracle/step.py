@@ -46,13 +46,13 @@ def step_sharded(tab: dict, hp, state: dict, grad: np.ndarray, master: np.ndarra
             scales[s] = np.float32(1.0)
             continue
         vr, vc = int(t["vrows"]), int(t["vcols"])
-        q, sc = quant.requant_block(master[s, :vr, :vc])
+        q, sc = quant.requant_block(master[s, :vr, :vc], getattr(hp, "scale_rule", 0))
         codes[s, :vr, :vc] = q
         scales[s] = sc
     return st, master, m, v, codes, scales
 
 
-def requant_param(p: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+def requant_param(p: np.ndarray, rule: int = 0) -> Tuple[np.ndarray, np.ndarray]:
     """Row-major [E, R, C] float32 -> (codes [E, R, C] uint8, scales [E, Rb, Cb] float32)."""
     e_n, r, c = p.shape
     _, rb, cb = grid(p.shape)
@@ -62,7 +62,7 @@ def requant_param(p: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
         for br in range(rb):
             for bc in range(cb):
                 sl = (e, slice(B * br, B * br + B), slice(B * bc, B * bc + B))
-                q, s = quant.requant_block(p[sl])
+                q, s = quant.requant_block(p[sl], rule)
                 codes[sl] = q
                 scales[e, br, bc] = s
     return codes, scales
@@ -84,5 +84,5 @@ def step_unsharded(hp, state: dict, grads: Dict[int, np.ndarray], masters: Dict[
     nm, nmm, nv, codes, scales = {}, {}, {}, {}, {}
     for p in pids:
         nm[p], nmm[p], nv[p] = optim.adamw(grads[p], masters[p], ms[p], vs[p], st, hp)
-        codes[p], scales[p] = requant_param(nm[p])
+        codes[p], scales[p] = requant_param(nm[p], getattr(hp, "scale_rule", 0))
     return st, nm, nmm, nv, codes, scales

@@ -39,6 +39,7 @@ class Hparams:
     growth_factor: float = 2.0
     backoff_factor: float = 0.5
     growth_interval: int = 1000
+    scale_rule: int = 0  # 0: amax / 448; 1: power of two (E8M0)
 
 
 @dataclass(frozen=True)
@@ -186,6 +187,11 @@ SMALL_WORKLOADS = {
     "ragged_small": Workload(
         name="ragged_small", shapes=ragged_shapes(1, 40, 64, 700, (1, 3)), dp=16,
         ranks=tuple(range(16)), steps=2, hp=TINY_HP, grad_sigma=1e-3),
+    "tiny_pow2": WORKLOADS["tiny"].with_(
+        name="tiny_pow2", hp=dataclasses.replace(TINY_HP, max_grad_norm=0.05, scale_rule=1)),
+    "ragged_small_pow2": Workload(
+        name="ragged_small_pow2", shapes=ragged_shapes(1, 40, 64, 700, (1, 3)), dp=16,
+        ranks=(0, 7, 15), steps=2, hp=dataclasses.replace(TINY_HP, scale_rule=1), grad_sigma=1e-3),
     "full_small": Workload(
         name="full_small", shapes=((4, 300, 520),), dp=1, ranks=(0,), steps=5,
         hp=dataclasses.replace(TINY_HP, max_grad_norm=1.0, loss_scaling=True, init_scale=65536.0),

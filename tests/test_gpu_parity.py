@@ -223,7 +223,8 @@ def _run_parity(w, ranks=None, fused=None, fold_on_read=False):
                     assert np.isnan(s[~blockmask[p]]).all()
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_clip", "tiny_lossscale", "dense_small", "moe_small", "full_small"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_clip", "tiny_lossscale", "dense_small", "moe_small", "full_small",
+                                  "tiny_pow2", "ragged_small_pow2"])
 @pytest.mark.parametrize("fold_on_read", [False, True])
 def test_step_parity(name, fold_on_read):
     _run_parity(synth.get(name), fold_on_read=fold_on_read)
@@ -315,3 +316,106 @@ def test_empty_and_degenerate_blocks():
                        hp=synth.Hparams(max_grad_norm=1.0), grad_sigma=0.0, master_sigma=0.0)
     _run_parity(w)
     _run_parity(w, fold_on_read=True)
+
+
+@pytest.mark.parametrize("name,split", [("tiny", "block"), ("ragged_small", "block"), ("ragged_small", "param"),
+                                        ("moe_small", "block"), ("dense_small", "block")])
+def test_all_ranks_gather_and_whole_buffer_unfold(name, split):
+    """Every rank steps its own shard; the ranks' folded FP8 codes and scales are
+    concatenated in rank order (what the all-gathers produce) and unfolded with the
+    table of the whole flat buffer.  The result equals the row-major definition."""
+    gh = _gh()
+    from blockwise_fp8_zero_fold_amd.shard import Shard
+    w = synth.get(name).with_(split=split)
+    steps = 2
+    ref, tabs = harness.run_sharded_all_ranks(w, steps=steps)
+    un = harness.run_unsharded(w, steps=steps)
+    sid = fz.SPLIT_PARAM if split == "param" else fz.SPLIT_BLOCK
+    dtype = fz.BF16 if w.master_dtype == "bf16" else fz.F32
+    codes_all, scales_all = [], []
+    for r in range(w.dp):
+        sh = Shard(w.shapes, w.dp, r, sid)
+        held = gh.held_experts(tabs[r]["entries"])
+        sh.init(fz.Hparams.make(w.hp), gh.master_tensors(w, held), dtype)
+        for t in range(1, steps + 1):
+            hp = fz.Hparams.make(w.hp, extra_sumsq=ref[r][t - 1]["extra"])
+            sh.update_rowmajor(hp, gh.grad_tensors(w, held, t))
+        codes_all.append(sh.fp8[: sh.n_slots * 16384])
+        scales_all.append(sh.scales[: sh.n_slots])
+    gathered = torch.cat(codes_all)
+    gscales = torch.cat(scales_all)
+    whole = fz.fp8z1_build_table(w.shapes, w.dp, fz.ALL_RANKS, sid)
+    assert whole.shard_slots * 16384 == gathered.numel()
+    dst = [torch.full(s, 0xA5, dtype=torch.uint8, device="cuda") for s in w.shapes]
+    dsc = [torch.full(otable.grid(s), float("nan"), dtype=torch.float32, device="cuda") for s in w.shapes]
+    fz.fp8z1_unfold(whole, gathered, fz.E4M3, gscales, dst, dsc)
+    torch.cuda.synchronize()
+    U = un[steps - 1]
+    for p in range(w.n_params):
+        assert gh.bits_equal(dst[p].cpu().numpy(), U["codes"][p]), (name, split, p)
+        assert gh.bits_equal(dsc[p].cpu().numpy(), U["scales"][p]), (name, split, p)
+
+
+def test_dequantize_every_code():
+    """All 256 codes times random scales (one per 128x128 block): float32 bit-exact
+    against the oracle, bfloat16 equal to torch's RNE cast of the oracle's float32."""
+    from oracle import quant as oquant
+    rng = np.random.default_rng(17)
+    shape = (2, 200, 300)
+    codes = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    codes[0, 0, :256] = np.arange(256, dtype=np.uint8)
+    scales = (2.0 ** rng.uniform(-20, 20, size=otable.grid(shape))).astype(np.float32)
+    want = oquant.dequantize(codes, scales)
+    dc, ds = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+    out = torch.empty(shape, dtype=torch.float32, device="cuda")
+    fz.fp8z1_dequantize(dc, ds, shape, fz.F32, out)
+    got = out.cpu().numpy()
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all()
+    assert got[~nan].tobytes() == want[~nan].tobytes()
+    ob = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    fz.fp8z1_dequantize(dc, ds, shape, fz.BF16, ob)
+    gb = ob.float().cpu().numpy()
+    wb = torch.from_numpy(want).to(torch.bfloat16).float().numpy()
+    assert (np.isnan(gb) == nan).all()
+    assert gb[~nan].tobytes() == wb[~nan].tobytes()
+
+
+@pytest.mark.parametrize("name", ["moe_small", "full_small"])
+def test_dequantized_weights_track_the_master(name):
+    """After a few steps the dequantized FP8 weights stay close to the FP32 master:
+    cosine > 0.995 per block and under 0.5% of real elements quantized to zero
+    (the health thresholds of the quantization-error table of the FP8-training page)."""
+    gh = _gh()
+    from blockwise_fp8_zero_fold_amd.shard import Shard
+    w = synth.get(name)
+    dtype = fz.BF16 if w.master_dtype == "bf16" else fz.F32
+    ref, tabs = harness.run_sharded_all_ranks(w, ranks=[0])
+    tab = tabs[0]
+    held = gh.held_experts(tab["entries"])
+    sh = Shard(w.shapes, w.dp, 0)
+    sh.init(fz.Hparams.make(w.hp), gh.master_tensors(w, held), dtype)
+    codes, scales = gh.code_tensors(w, held)
+    for t in range(1, w.steps + 1):
+        sh.step(fz.Hparams.make(w.hp, extra_sumsq=ref[0][t - 1]["extra"]), gh.grad_tensors(w, held, t), codes, scales,
+                fold_on_read=True)
+    masters = [torch.full(s, float("nan"), dtype=torch.float32, device="cuda") if p in held else None
+               for p, s in enumerate(w.shapes)]
+    fz.fp8z1_unfold(sh.table, sh.master, fz.F32, None, masters)
+    zeros = total = 0
+    worst = 1.0
+    for p in held:
+        deq = torch.empty(w.shapes[p], dtype=torch.float32, device="cuda")
+        fz.fp8z1_dequantize(codes[p], scales[p], w.shapes[p], fz.F32, deq)
+        mask = torch.from_numpy(np.isin(np.arange(w.shapes[p][0]), held[p])).cuda()
+        a, b = deq[mask].double(), masters[p][mask].double()
+        E, R, C = a.shape
+        for br in range(0, R, 128):
+            for bc in range(0, C, 128):
+                x, y = a[:, br:br + 128, bc:bc + 128], b[:, br:br + 128, bc:bc + 128]
+                cos = (x * y).sum(dim=(1, 2)) / (x.norm(dim=(1, 2)) * y.norm(dim=(1, 2)))
+                worst = min(worst, float(cos.min()))
+        zeros += int((codes[p][mask] & 0x7F).eq(0).sum())
+        total += a.numel()
+    assert worst > 0.995, worst
+    assert zeros / total < 0.005, zeros / total

@@ -11,13 +11,13 @@ import synth
 from oracle import table as otable
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "fp8z1.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include"))) if h.endswith(".h")]
 
 fz = pytest.importorskip("blockwise_fp8_zero_fold_amd", reason="libfp8z1.so not built")
 
 
 def _declared():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fp8z1_[a-z0-9_]+)\s*\(", text)))
 
@@ -112,6 +112,9 @@ def test_argument_errors_before_any_gpu_work():
         fz.fp8z1_step(t, hp_clip, 16, 16, 16, 16, 16, 16, 16, stream=0)
     with pytest.raises(fz.Fp8z1Error, match="workspace"):
         fz.fp8z1_step(t, hp_clip, 16, 16, 16, 16, 16, 16, 16, workspace=16, workspace_bytes=8, stream=0)
+    hp_rule = fz.Hparams.make(synth.Hparams(scale_rule=5))
+    with pytest.raises(fz.Fp8z1Error, match="scale_rule"):
+        fz.fp8z1_step(t, hp_rule, 16, 16, 16, 16, 16, 16, 16, stream=0)
     hp_bad = fz.Hparams.make(synth.Hparams(beta1=1.0))
     with pytest.raises(fz.Fp8z1Error, match="betas"):
         fz.fp8z1_step(t, hp_bad, 16, 16, 16, 16, 16, 16, 16, stream=0)

@@ -80,3 +80,15 @@ def test_ulp_distance():
     a = np.array([0x00, 0x80, 0x01, 0x81, 0x7E, 0x7F, 0x10], dtype=np.uint8)
     b = np.array([0x80, 0x00, 0x02, 0x01, 0x7D, 0xFF, 0x10], dtype=np.uint8)
     assert e4m3.ulp_distance(a, b).tolist() == [0, 0, 1, 2, 1, 0, 0]
+
+
+def test_decode_matches_torch_float8():
+    """Every code's value equals torch's float8_e4m3fn -> float32 conversion."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = e4m3.decode(codes)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == ref[~nan]).all()
+    assert (np.signbit(got[~nan]) == np.signbit(ref[~nan])).all()

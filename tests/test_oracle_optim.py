@@ -229,3 +229,51 @@ def test_quantization_health_on_synthetic_weights():
         cos.append(float(np.dot(d.ravel(), b.ravel()) / (np.linalg.norm(d) * np.linalg.norm(b))))
     assert zeros / x.size < 0.005
     assert min(cos) > 0.995
+
+
+def test_dequantize_closed_forms():
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 2, 128)
+    one = np.ones((1, 1, 1), np.float32)
+    d = quant.dequantize(codes, one)
+    ref = e4m3.decode(codes)
+    assert (np.isnan(d) == np.isnan(ref)).all() and (d[~np.isnan(d)] == ref[~np.isnan(ref)]).all()
+    for k in (-40, -3, 0, 7, 30):  # a power-of-two scale only moves the exponent
+        d2 = quant.dequantize(codes, np.full((1, 1, 1), 2.0 ** k, np.float32))
+        fin = ~np.isnan(ref)
+        assert (d2[fin] == (ref[fin] * 2.0 ** k).astype(np.float32)).all()
+    # round trip: dequantize(requant(x)) is within half an E4M3 step of x, in units of the scale
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((1, 256, 384)) * 0.02).astype(np.float32)
+    from oracle import step as ostep
+    c, s = ostep.requant_param(x)
+    y = quant.dequantize(c, s).astype(np.float64)
+    sfull = np.repeat(np.repeat(s, 128, axis=1), 128, axis=2).astype(np.float64)
+    q = x / sfull
+    assert np.all(np.abs(y - x) <= sfull * (_quantum(q) / 2 + 1e-6 * np.abs(q)))
+
+
+def test_pow2_scale_closed_forms():
+    """E8M0 rule: 2^(floor(log2 amax) - 8), clamped at 2^-127; 0 -> 1; inf -> inf."""
+    f = np.float32
+    cases = {1.0: 2.0 ** -8, 448.0: 1.0, 500.0: 1.0, 511.9: 1.0, 512.0: 2.0, 0.75: 2.0 ** -9, 2.0 ** -100: 2.0 ** -108,
+             2.0 ** -125: 2.0 ** -127, 1e-45: 2.0 ** -127, 3.0e38: 2.0 ** 119}
+    for amax, want in cases.items():
+        assert quant.block_scale(f(amax), quant.SCALE_POW2) == f(want), amax
+    assert quant.block_scale(f(0.0), quant.SCALE_POW2) == 1.0
+    assert np.isinf(quant.block_scale(f(np.inf), quant.SCALE_POW2))
+
+
+def test_pow2_scale_requant_invariants():
+    rng = np.random.default_rng(23)
+    for _ in range(200):
+        x = (rng.standard_normal((64, 96)) * 10.0 ** rng.uniform(-30, 30)).astype(np.float32)
+        c, s = quant.requant_block(x, quant.SCALE_POW2)
+        m, e = np.frexp(np.float64(s))
+        assert m == 0.5, "a power of two"
+        amax = np.max(np.abs(x).astype(np.float64))
+        if s > 2.0 ** -127:
+            assert 256.0 <= amax / s < 512.0
+            # the largest element saturates or lands on 256..448
+            assert np.max(c & 0x7F) >= 0x78
+        # dividing by a power of two is exact: the codes are those of x * 2^-k
+        assert (c == e4m3.encode((x.astype(np.float64) / np.float64(s)).astype(np.float32))).all()

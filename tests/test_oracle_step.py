@@ -29,7 +29,8 @@ def _compare_all_ranks(w):
     return un, sh
 
 
-@pytest.mark.parametrize("name", ["tiny", "tiny_clip", "tiny_lossscale", "dense_small", "moe_small", "full_small"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_clip", "tiny_lossscale", "dense_small", "moe_small", "full_small",
+                                  "tiny_pow2", "ragged_small_pow2"])
 def test_sharded_equals_unsharded(name):
     _compare_all_ranks(synth.get(name))
 
