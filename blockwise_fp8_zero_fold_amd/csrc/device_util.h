@@ -93,6 +93,25 @@ __device__ __forceinline__ void st_stream(uint4* p, uint4 x) {
 }
 __device__ __forceinline__ void st_stream(uint32_t* p, uint32_t x) { __builtin_nontemporal_store(x, p); }
 
+// 16-byte accesses at addresses that are only element-aligned (a row of a
+// row-major param whose width is not a multiple of 4).  gfx950 under ROCm runs
+// in unaligned-access mode, so these are single dwordx4 instructions (the
+// compiler emits them for these types); the callers only use them on bytes that
+// lie inside the row segment they own.
+typedef float v4f_a4_t __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ __forceinline__ float4 ld_stream_a4(const float* p) {
+  const v4f_a4_t r = __builtin_nontemporal_load(reinterpret_cast<const v4f_a4_t*>(p));
+  return make_float4(r.x, r.y, r.z, r.w);
+}
+__device__ __forceinline__ float4 ld_a4(const float* p) {
+  float4 r;
+  __builtin_memcpy(&r, p, 16);
+  return r;
+}
+__device__ __forceinline__ void st_a4(float* p, float4 x) { __builtin_memcpy(p, &x, 16); }
+__device__ __forceinline__ void st_a1(uint8_t* p, uint4 x) { __builtin_memcpy(p, &x, 16); }
+
 // Square of a float32 value in float64 (exact: a 24-bit significand squared fits in 53 bits).
 __device__ __forceinline__ double sq64(float x) {
   const double d = static_cast<double>(x);

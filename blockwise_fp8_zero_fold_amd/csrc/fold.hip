@@ -6,10 +6,10 @@
 // swaps the block-column index with the row-within-block index, so each
 // 128-element row segment of the source moves whole to a contiguous 512-byte
 // destination.  The kernel is therefore a segment gather, not a transpose:
-// one workgroup per slot, 32 lanes per row segment, 16-byte loads and stores
-// when the source rows are 16-byte aligned (C % 4 == 0 for float32), element
-// loads with masks otherwise.  Every source byte is read once, every
-// destination byte written once.
+// one workgroup per slot, 32 lanes per row segment, 16-byte loads (at any
+// element alignment of the source rows) and 16-byte stores; in a partial block
+// only the chunk across the last real column is loaded element by element.
+// Every source byte is read once, every destination byte written once.
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"
@@ -22,18 +22,19 @@ constexpr int kPasses = kChunks / kFoldThreads;
 
 template <typename T>
 struct Src;
+// load4: four consecutive elements from an element-aligned address (one vector
+// load; see device_util.h), load1: one element
 template <>
 struct Src<float> {
-  static constexpr int kAlign = 16;
-  __device__ static float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  __device__ static float4 load4(const float* p) { return ld_a4(p); }
   __device__ static float load1(const float* p) { return *p; }
 };
 template <>
 struct Src<uint16_t> {  // bfloat16 bits
-  static constexpr int kAlign = 8;
   __device__ static float widen(uint32_t b) { return __uint_as_float(b << 16); }
   __device__ static float4 load4(const uint16_t* p) {
-    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    uint2 u;
+    __builtin_memcpy(&u, p, 8);
     return make_float4(widen(u.x & 0xffffu), widen(u.x >> 16), widen(u.y & 0xffffu), widen(u.y >> 16));
   }
   __device__ static float load1(const uint16_t* p) { return widen(*p); }
@@ -62,26 +63,30 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(const SlotPlan* __re
     const T* src = static_cast<const T*>(srcs[P.param]) + P.off;
     const int64_t ld = P.ld;
     const int vr = P.vr, vc = P.vc;
-    const bool fast = vr == kB && vc == kB && (ld % 4) == 0 &&
-                      (reinterpret_cast<uintptr_t>(src) % Src<T>::kAlign) == 0;
     float4 x[kPasses];
-    if (fast) {
+    if (vr == kB && vc == kB) {
 #pragma unroll
       for (int k = 0; k < kPasses; ++k) {
         const int c = t + kFoldThreads * k;
         x[k] = Src<T>::load4(src + (c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow));
       }
     } else {
+      // partial block: whole chunks inside the real region load as vectors, the
+      // chunk across the last real column element by element, the rest is padding
 #pragma unroll
       for (int k = 0; k < kPasses; ++k) {
         const int c = t + kFoldThreads * k;
         const int i = c / kChunksPerRow, j = 4 * (c % kChunksPerRow);
         const T* row = src + i * ld + j;
-        const bool rv = i < vr;
-        x[k].x = (rv && j + 0 < vc) ? Src<T>::load1(row + 0) : 0.f;
-        x[k].y = (rv && j + 1 < vc) ? Src<T>::load1(row + 1) : 0.f;
-        x[k].z = (rv && j + 2 < vc) ? Src<T>::load1(row + 2) : 0.f;
-        x[k].w = (rv && j + 3 < vc) ? Src<T>::load1(row + 3) : 0.f;
+        if (i < vr && j + 4 <= vc) {
+          x[k] = Src<T>::load4(row);
+        } else {
+          const bool rv = i < vr;
+          x[k].x = (rv && j + 0 < vc) ? Src<T>::load1(row + 0) : 0.f;
+          x[k].y = (rv && j + 1 < vc) ? Src<T>::load1(row + 1) : 0.f;
+          x[k].z = (rv && j + 2 < vc) ? Src<T>::load1(row + 2) : 0.f;
+          x[k].w = (rv && j + 3 < vc) ? Src<T>::load1(row + 3) : 0.f;
+        }
       }
     }
 #pragma unroll

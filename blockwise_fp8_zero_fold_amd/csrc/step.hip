@@ -219,16 +219,16 @@ struct GradSrc {
   const float4* folded;  // this slot's folded grads (!ROWMAJOR)
   const float* rows;     // element (0, 0) of this slot's block (ROWMAJOR)
   int64_t ld;            // row stride (ROWMAJOR)
-  bool vec;              // rows are 16-byte aligned (ROWMAJOR)
 
+  // the 4 elements of chunk c (all real)
   __device__ __forceinline__ float4 chunk(int c) const {
     if (!ROWMAJOR) return ld_stream(folded + c);
-    return ld_stream(reinterpret_cast<const float4*>(rows + (c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow)));
+    return ld_stream_a4(rows + (c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow));
   }
   // elements j .. j+3 of row i, those at columns >= vc read as 0
   __device__ __forceinline__ void chunk_masked(int c, int i, int j, int vc, float g[4]) const {
-    if (!ROWMAJOR || (vec && j + 4 <= vc)) {
-      const float4 x = ROWMAJOR ? *reinterpret_cast<const float4*>(rows + i * ld + j) : folded[c];
+    if (!ROWMAJOR || j + 4 <= vc) {
+      const float4 x = ROWMAJOR ? ld_stream_a4(rows + i * ld + j) : ld_stream(folded + c);
       g[0] = x.x;
       g[1] = x.y;
       g[2] = x.z;
@@ -268,12 +268,10 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
     G.folded = nullptr;
     G.rows = static_cast<const float*>(grad_rows[P.param]) + P.off;
     G.ld = P.ld;
-    G.vec = (P.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(G.rows) % 16) == 0;
   } else {
     G.folded = reinterpret_cast<const float4*>(grad) + base;
     G.rows = nullptr;
     G.ld = 0;
-    G.vec = true;
   }
   float4* p4 = reinterpret_cast<float4*>(master) + base;
   float4* m4 = reinterpret_cast<float4*>(mom1) + base;
@@ -283,7 +281,7 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
   float amax = 0.0f;
   const int vr = P.vr, vc = P.vc;
   const bool full = vr == kB && vc == kB;
-  if (full && G.vec) {
+  if (full) {
 #pragma unroll
     for (int q = 0; q < kUpdPasses; ++q) {
       const int c = t + kUpdThreads * q;
@@ -299,9 +297,8 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
       amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e0.p), fabsf(e1.p)), fmaxf(fabsf(e2.p), fabsf(e3.p))));
     }
   } else {
-    // partial block (or rows that are not 16-byte aligned): padding positions
-    // are neither used nor changed (their loaded values are written back as
-    // they were) and count 0 in amax
+    // partial block: padding positions are neither used nor changed (their
+    // loaded values are written back as they were) and count 0 in amax
 #pragma unroll
     for (int q = 0; q < kUpdPasses; ++q) {
       const int c = t + kUpdThreads * q;

@@ -5,12 +5,11 @@
 //
 // As in the fold, whole row segments move (no element transpose).  FP8
 // codes: four workgroups per slot, each a quarter of the block; a 128-byte row
-// segment is 8 lanes of 16-byte streaming stores when the destination rows are 16-byte
-// aligned and the block has all 128 columns; otherwise the rows are staged in
-// LDS and written with aligned 4-byte stores plus single bytes at the row
-// ends, which never touch a byte that belongs to a neighbouring block.
-// float32 (used for round-trip checks): one workgroup per slot, 16-byte or
-// 4-byte stores.
+// segment is 8 lanes of 16-byte stores (streaming when the row is 16-byte
+// aligned, plain unaligned stores otherwise); in a partial block the chunk
+// across the last real column is written byte by byte, so no byte of a
+// neighbouring block's row is ever written.  float32 (used for round-trip
+// checks): one workgroup per slot, the same with 4-element chunks.
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"
@@ -24,14 +23,12 @@ constexpr int kUnfThreads = 256;
 // 4 KB), so that the workgroups in flight cover a compact range of memory.
 constexpr int kUnfRows = 32;
 constexpr int kUnfParts = kB / kUnfRows;
-constexpr int kUnfWordsPerRow = (3 + kB + 3) / 4;  // 4-byte words touched by a 128-byte row at any alignment
 
 __global__ __launch_bounds__(kUnfThreads) void unfold_e4m3_kernel(const SlotPlan* __restrict__ plan,
                                                                   const uint8_t* __restrict__ folded,
                                                                   void* const* __restrict__ dsts,
                                                                   const float* __restrict__ scales,
                                                                   float* const* __restrict__ dscales) {
-  __shared__ uint32_t stage[kUnfRows * kB / 4 + 4];  // the part's rows, plus one word of slack per row end
   const int64_t s = blockIdx.x / kUnfParts;
   const int part = blockIdx.x % kUnfParts;
   const SlotPlan P = plan[s];
@@ -40,42 +37,22 @@ __global__ __launch_bounds__(kUnfThreads) void unfold_e4m3_kernel(const SlotPlan
   if (dscales && part == 0 && t == 0) dscales[P.param][P.soff] = scales[s];
   const int vr = P.vr, vc = P.vc;
   const int r0 = part * kUnfRows;
-  if (r0 >= vr) return;
-  const int nrows = min(kUnfRows, vr - r0);
+  const int i = t >> 3, j = 16 * (t & 7);  // 8 lanes per 128-byte row, one 16-byte chunk each
+  if (r0 + i >= vr || j >= vc) return;
   const int64_t ld = P.ld;
-  uint8_t* dst = static_cast<uint8_t*>(dsts[P.param]) + P.off + r0 * ld;
-  const uint4* src = reinterpret_cast<const uint4*>(folded + s * kBlockElems + r0 * kB);
-  if (vc == kB && (ld % 16) == 0 && (reinterpret_cast<uintptr_t>(dst) % 16) == 0) {
-    // 8 lanes per 128-byte row, one 16-byte load and store per lane
-    const int i = t >> 3;
-    if (i < nrows) st_stream(reinterpret_cast<uint4*>(dst + i * ld + 16 * (t & 7)), ld_stream(src + t));
-    return;
-  }
-  // Rows that are not 16-byte aligned, or shorter than 128 bytes: stage the rows
-  // in LDS, then write each destination row with aligned 4-byte stores inside
-  // the row and single bytes in the (at most two) words it shares with the
-  // neighbouring blocks, so no byte outside the row is written.
-  if (t < nrows * (kB / 16)) reinterpret_cast<uint4*>(stage)[t] = src[t];
-  if (t < 4) stage[kUnfRows * kB / 4 + t] = 0u;
-  __syncthreads();
-  const uint8_t* sb = reinterpret_cast<const uint8_t*>(stage);
-  for (int f = t; f < nrows * kUnfWordsPerRow; f += kUnfThreads) {
-    const int i = f / kUnfWordsPerRow, w = f % kUnfWordsPerRow;
-    uint8_t* row = dst + i * ld;
-    const int head = static_cast<int>(reinterpret_cast<uintptr_t>(row) & 3u);
-    const int o = 4 * w - head;  // row offset of this word's first byte; row + o is 4-byte aligned
-    if (o >= vc) continue;
-    if (o >= 0 && o + 4 <= vc) {
-      const uint32_t lo = stage[i * (kB / 4) + (o >> 2)];
-      const uint32_t hi = stage[i * (kB / 4) + (o >> 2) + 1];
-      *reinterpret_cast<uint32_t*>(row + o) = __builtin_amdgcn_alignbyte(hi, lo, static_cast<uint32_t>(o & 3));
-    } else {
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int ob = o + b;
-        if (ob >= 0 && ob < vc) row[ob] = sb[i * kB + ob];
-      }
-    }
+  uint8_t* row = static_cast<uint8_t*>(dsts[P.param]) + P.off + (r0 + i) * ld;
+  const uint4 x = ld_stream(reinterpret_cast<const uint4*>(folded + s * kBlockElems + (r0 + i) * kB + j));
+  if (j + 16 <= vc) {
+    // a chunk inside the row: one 16-byte store, at any alignment of the row
+    if ((reinterpret_cast<uintptr_t>(row + j) & 15u) == 0)
+      st_stream(reinterpret_cast<uint4*>(row + j), x);
+    else
+      st_a1(row + j, x);
+  } else {
+    // the chunk across the last real column: its real bytes one by one, so no
+    // byte of the neighbouring block's row is written
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    for (int b = 0; b < vc - j; ++b) row[j + b] = static_cast<uint8_t>(w[b >> 2] >> (8 * (b & 3)));
   }
 }
 
@@ -93,18 +70,19 @@ __global__ __launch_bounds__(kUnfThreads) void unfold_f32_kernel(const SlotPlan*
   const float* src = folded + s * kBlockElems;
   const int64_t ld = P.ld;
   const int vr = P.vr, vc = P.vc;
-  if (vc == kB && (ld % 4) == 0 && (reinterpret_cast<uintptr_t>(dst) % 16) == 0) {
-    const float4* s4 = reinterpret_cast<const float4*>(src);
+  const float4* s4 = reinterpret_cast<const float4*>(src);
 #pragma unroll 4
-    for (int q = 0; q < kChunks / kUnfThreads; ++q) {
-      const int c = t + kUnfThreads * q;
-      const int i = c / kChunksPerRow;
-      if (i < vr) *reinterpret_cast<float4*>(dst + i * ld + 4 * (c % kChunksPerRow)) = s4[c];
-    }
-  } else {
-    for (int idx = t; idx < kBlockElems; idx += kUnfThreads) {
-      const int i = idx >> 7, j = idx & 127;
-      if (i < vr && j < vc) dst[i * ld + j] = src[idx];
+  for (int q = 0; q < kChunks / kUnfThreads; ++q) {
+    const int c = t + kUnfThreads * q;
+    const int i = c / kChunksPerRow, j = 4 * (c % kChunksPerRow);
+    if (i >= vr || j >= vc) continue;
+    float* d = dst + i * ld + j;
+    const float4 x = s4[c];
+    if (j + 4 <= vc) {
+      st_a4(d, x);
+    } else {
+      const float e[4] = {x.x, x.y, x.z, x.w};
+      for (int b = 0; b < vc - j; ++b) d[b] = e[b];
     }
   }
 }
