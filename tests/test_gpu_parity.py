@@ -155,6 +155,8 @@ def _bar(got, want, what):
 
 
 def _codes_bar(got, want, what):
+    if got.size == 0:  # a shard of padding slots only
+        return
     d = oe4m3.ulp_distance(got, want)
     assert d.max() <= 1, f"{what}: code distance {d.max()}"
     assert (d > 0).mean() <= 1e-4, f"{what}: {(d > 0).mean()} of codes differ by 1 ulp"
@@ -419,3 +421,22 @@ def test_dequantized_weights_track_the_master(name):
         total += a.numel()
     assert worst > 0.995, worst
     assert zeros / total < 0.005, zeros / total
+
+
+def test_extreme_shapes_and_all_padding_ranks():
+    """Widest and tallest params the 16-bit block indices allow (65,536 block columns /
+    rows, one real row / column per block), and more ranks than blocks (ranks whose
+    shard is all padding slots)."""
+    wide = synth.Workload(name="extreme", shapes=((1, 1, (1 << 23) - 1), (1, (1 << 23) - 1, 1)), dp=64,
+                          ranks=(0, 31, 63), steps=1, hp=synth.Hparams(max_grad_norm=1.0), grad_sigma=1e-3)
+    tabs = {r: otable.build(wide.shapes, wide.dp, r) for r in wide.ranks}
+    ent = np.concatenate([tabs[r]["entries"] for r in wide.ranks])
+    assert ent["bcol"].max() == 65535 and ent["brow"].max() == 65535
+    assert ent["vcols"].min() == 1 and ent["vrows"].min() == 1
+    _run_parity(wide)
+    _run_parity(wide, fold_on_read=True)
+    few = synth.Workload(name="few_blocks", shapes=((1, 130, 70),), dp=16, ranks=(0, 1, 2, 15), steps=2,
+                         hp=synth.Hparams(max_grad_norm=1.0), grad_sigma=1e-3)
+    assert (otable.build(few.shapes, few.dp, 15)["entries"]["param"] < 0).all()
+    _run_parity(few)
+    _run_parity(few, fold_on_read=True)
