@@ -297,14 +297,21 @@ def main() -> int:
     pat_bytes = 29 * nslots * BLOCK
     t_copy = ev_time(lambda: fz.fp8z1_probe_copy(probe_bufs[0], probe_bufs[1]), 10)
     copy_bytes = 2 * probe_bufs[0].numel() * 4
+    # the same copy with the workgroups in flight spread over S far-apart ranges
+    tiles = probe_bufs[0].numel() * 4 // 4096
+    spread_gbs = {}
+    for S in (1, 16, 64, 256, 1024):
+        if tiles % S == 0:
+            spread_gbs[S] = copy_bytes / ev_time(lambda: fz.fp8z1_probe_copy(probe_bufs[0], probe_bufs[1], S), 10) / 1e9
     del probe_bufs, probe_codes
     torch.cuda.empty_cache()
     ceiling = {"update_pattern_gbs": pat_bytes / t_pat / 1e9, "copy_gbs": copy_bytes / t_copy / 1e9,
                "update_vs_pattern": achieved / (pat_bytes / t_pat / 1e9),
+               "copy_gbs_by_spread": spread_gbs,
                "note": "same-run streaming references: fp8z1_probe_update_pattern (the update's loads and stores, "
                        "no arithmetic, same slot count) and fp8z1_probe_copy (plain copy, 4 KB per workgroup)"}
-    print(f"# ceilings: update pattern {ceiling['update_pattern_gbs']:.0f} GB/s, copy {ceiling['copy_gbs']:.0f} GB/s",
-          file=sys.stderr, flush=True)
+    print(f"# ceilings: update pattern {ceiling['update_pattern_gbs']:.0f} GB/s, copy {ceiling['copy_gbs']:.0f} GB/s, "
+          f"copy by spread {({k: round(v) for k, v in spread_gbs.items()})}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -97,7 +97,7 @@ _sig = {
     "fp8z1_state_write": (C.c_int, [_vp, C.POINTER(State), _vp]),
     "fp8z1_encode_e4m3": (C.c_int, [_vp, _vp, C.c_int64, _vp]),
     "fp8z1_dequantize": (C.c_int, [_vp, _vp, C.c_int64, C.c_int64, C.c_int64, C.c_int32, _vp, _vp]),
-    "fp8z1_probe_copy": (C.c_int, [_vp, _vp, C.c_int64, _vp]),
+    "fp8z1_probe_copy": (C.c_int, [_vp, _vp, C.c_int64, C.c_int64, _vp]),
     "fp8z1_probe_update_pattern": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int64, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
@@ -330,10 +330,10 @@ def fp8z1_dequantize(codes, scales, shape, out_dtype: int, out, stream=None) -> 
            "fp8z1_dequantize")
 
 
-def fp8z1_probe_copy(src, dst, stream=None) -> None:
+def fp8z1_probe_copy(src, dst, spread: int = 1, stream=None) -> None:
     n = src.numel() * src.element_size()
     _need(dst, n, "probe_copy dst")
-    _check(lib.fp8z1_probe_copy(_ptr(src), _ptr(dst), n, _stream(stream)), "fp8z1_probe_copy")
+    _check(lib.fp8z1_probe_copy(_ptr(src), _ptr(dst), n, spread, _stream(stream)), "fp8z1_probe_copy")
 
 
 def fp8z1_probe_update_pattern(g, p, m, v, codes, nslots: int, stream=None) -> None:

@@ -10,9 +10,15 @@
 namespace fp8z1 {
 namespace {
 
-// plain copy, 4 KB per workgroup (256 lanes x 16 bytes), streaming accesses
-__global__ __launch_bounds__(256) void probe_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+// plain copy, 4 KB per workgroup (256 lanes x 16 bytes), streaming accesses.
+// spread = 1: workgroup b copies tile b, so the workgroups in flight cover one
+// compact range; spread = S > 1: tile (b % S) * (ntiles / S) + b / S, so they
+// cover S far-apart ranges, each walked in order
+__global__ __launch_bounds__(256) void probe_copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst,
+                                                         int64_t ntiles, int64_t spread) {
+  const int64_t b = blockIdx.x;
+  const int64_t tile = spread == 1 ? b : (b % spread) * (ntiles / spread) + b / spread;
+  const int64_t i = tile * 256 + threadIdx.x;
   st_stream(dst + i, ld_stream(src + i));
 }
 
@@ -44,15 +50,18 @@ __global__ __launch_bounds__(256) void probe_update_kernel(const float4* __restr
 
 using namespace fp8z1;
 
-extern "C" int fp8z1_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+extern "C" int fp8z1_probe_copy(const void* src, void* dst, int64_t bytes, int64_t spread, void* stream) {
   if (!src || !dst || bytes < 0 || bytes % 4096 || reinterpret_cast<uintptr_t>(src) % 16 ||
       reinterpret_cast<uintptr_t>(dst) % 16)
     return set_error(FP8Z1_EINVAL, "probe_copy: bytes must be a multiple of 4096, buffers 16-byte aligned");
   const int64_t blocks = bytes / 4096;
+  if (spread < 1 || blocks % spread)
+    return set_error(FP8Z1_EINVAL, "probe_copy: spread must be >= 1 and divide bytes / 4096");
   if (blocks == 0) return FP8Z1_OK;
   if (blocks > 0x7fffffff) return set_error(FP8Z1_EINVAL, "probe_copy: too large");
   hipLaunchKernelGGL(probe_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(src), static_cast<uint4*>(dst));
+                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(src), static_cast<uint4*>(dst),
+                     blocks, spread);
   return check_hip(hipGetLastError(), "probe_copy: launch");
 }
 

@@ -18,8 +18,13 @@ extern "C" {
 #endif
 
 /* Copy `bytes` (a multiple of 4096) from src to dst, 4 KB per workgroup,
- * 16-byte streaming loads and stores.  Both buffers 16-byte aligned. */
-int fp8z1_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+ * 16-byte streaming loads and stores.  Both buffers 16-byte aligned.
+ * spread = 1: workgroup b copies the b-th 4 KB tile, so the workgroups in
+ * flight cover one compact range of memory; spread = S (dividing the tile
+ * count): workgroup b copies tile (b % S) * (tiles / S) + b / S, so they cover
+ * S far-apart ranges at once (the traffic shape of kernels whose workgroups
+ * each own a large contiguous block). */
+int fp8z1_probe_copy(const void* src, void* dst, int64_t bytes, int64_t spread, void* stream);
 
 /* The update kernel's traffic over nslots 128x128 slots: per slot, read 64 KB
  * of each of g, p, m, v and write 64 KB of each of p, m, v plus 16 KB of

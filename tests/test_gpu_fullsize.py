@@ -64,7 +64,7 @@ def _slab_sumsq(ent, slab, p, e):
     return sel, tot
 
 
-@pytest.mark.parametrize("name,steps", [("moe", 5), ("dense", 3), ("full", 4), ("ragged", 2)])
+@pytest.mark.parametrize("name,steps", [("moe", 5), ("dense", 10), ("full", 5), ("ragged", 3)])
 @pytest.mark.parametrize("fold_on_read", [True, False])
 def test_full_size_sampled(name, steps, fold_on_read):
     fz = _fz()
