@@ -70,6 +70,13 @@ def build(verbose: bool = False) -> str:
     tmp = OUT + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, OUT)
+    # a C-ABI consumer without Python or torch, used by the GPU tests
+    example = os.path.join(ROOT, "tests", "native", "abi_c_step.cpp")
+    if os.path.exists(example):
+        exe = os.path.join(ROOT, "tests", "native", "abi_c_step")
+        _run([HIPCC, "-O2", "-std=c++17", example, "-L" + PKG, "-lfp8z1",
+              "-Wl,-rpath,$ORIGIN/../../blockwise_fp8_zero_fold_amd", "-o", exe + ".tmp"])
+        os.replace(exe + ".tmp", exe)
     return OUT
 
 

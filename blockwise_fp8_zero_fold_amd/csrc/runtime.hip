@@ -40,18 +40,22 @@ int ensure_device(fp8z1_table* t) {
     p.vr = e.vrows;
     p.vc = e.vcols;
   }
+  // (a failed earlier attempt may have left some of these allocated: keep them)
   for (int r = 0; r < kNumRoles; ++r) {
     PtrCache& c = t->ptrs[r];
     const size_t bytes = sizeof(void*) * t->shapes.size();
-    rc = check_hip(hipHostMalloc(reinterpret_cast<void**>(&c.host), bytes, hipHostMallocDefault), "hipHostMalloc");
-    if (!rc) rc = check_hip(hipMalloc(reinterpret_cast<void**>(&c.dev), bytes), "hipMalloc");
-    if (!rc) rc = check_hip(hipEventCreateWithFlags(reinterpret_cast<hipEvent_t*>(&c.done), hipEventDisableTiming),
-                            "hipEventCreate");
+    if (!c.host)
+      rc = check_hip(hipHostMalloc(reinterpret_cast<void**>(&c.host), bytes, hipHostMallocDefault), "hipHostMalloc");
+    if (!rc && !c.dev) rc = check_hip(hipMalloc(reinterpret_cast<void**>(&c.dev), bytes), "hipMalloc");
+    if (!rc && !c.done)
+      rc = check_hip(hipEventCreateWithFlags(reinterpret_cast<hipEvent_t*>(&c.done), hipEventDisableTiming),
+                     "hipEventCreate");
     if (rc) return rc;
     c.valid = false;
   }
   if (n) {
-    rc = check_hip(hipMalloc(reinterpret_cast<void**>(&t->d_plan), n * sizeof(SlotPlan)), "hipMalloc(plan)");
+    if (!t->d_plan)
+      rc = check_hip(hipMalloc(reinterpret_cast<void**>(&t->d_plan), n * sizeof(SlotPlan)), "hipMalloc(plan)");
     if (rc) return rc;
     rc = check_hip(hipMemcpy(t->d_plan, plan.data(), n * sizeof(SlotPlan), hipMemcpyHostToDevice), "hipMemcpy(plan)");
     if (rc) return rc;

@@ -33,6 +33,10 @@
  *   - A table is bound to the device current at its first GPU use.  All GPU
  *     calls that use one table must be issued on one stream, or ordered by
  *     the caller; calls on distinct tables are independent and thread-safe.
+ *     fp8z1_table_free waits for the device to finish before releasing.
+ *   - Rows of row-major arrays may start at any element alignment: kernels
+ *     use 16-byte accesses (gfx950 runs in unaligned-access mode) but never
+ *     touch a byte outside the block row segment they own.
  *   - Layouts: a param is row-major [E, R, C] (a 2-D param has E = 1).
  *     A folded shard is shard_slots blocks of 128 x 128 elements, each block
  *     row-major, blocks in table order; padding positions are +0.
@@ -155,9 +159,10 @@ int fp8z1_table_entries(const fp8z1_table* table, const fp8z1_block** entries);
 void fp8z1_table_free(fp8z1_table* table);
 
 /* Fold (section "参数布局变换"): gather the shard's blocks from row-major
- * params into dst (device, shard_slots*16384 float32), widening BF16 to
- * float32 exactly.  src: host array of n_params device pointers to row-major
- * [E,R,C] params of type src_dtype (FP8Z1_F32 or FP8Z1_BF16), 4-byte aligned;
+ * params into dst (device, shard_slots*16384 float32, 16-byte aligned),
+ * widening BF16 to float32 exactly.  src: host array of n_params device
+ * pointers to row-major [E,R,C] params of type src_dtype (FP8Z1_F32 or
+ * FP8Z1_BF16), aligned to their element size (rows need not be 16-byte aligned);
  * an entry may be NULL if the shard holds no block of that param.  Padding
  * positions and padding slots are written +0.  Used on the FP32/BF16
  * weights at init and on the reduced FP32 grads every step.

@@ -440,3 +440,49 @@ def test_extreme_shapes_and_all_padding_ranks():
     assert (otable.build(few.shapes, few.dp, 15)["entries"]["param"] < 0).all()
     _run_parity(few)
     _run_parity(few, fold_on_read=True)
+
+
+def test_c_abi_consumer_without_python(tmp_path):
+    """A C++ program (tests/native/abi_c_step.cpp, built with the library) drives the
+    ABI with its own HIP allocations and stream, no torch in the process; its outputs
+    equal the oracle's."""
+    import subprocess
+    exe = os.path.join(os.path.dirname(__file__), "native", "abi_c_step")
+    if not os.path.exists(exe):
+        pytest.fail("tests/native/abi_c_step is not built (blockwise_fp8_zero_fold_amd/build.py builds it)")
+    w = synth.get("tiny_clip")
+    rank = 1
+    ref, tabs = harness.run_sharded_all_ranks(w, ranks=[rank])
+    un = harness.run_unsharded(w)
+    P = harness.masters(w)
+    hp = w.hp
+    with open(tmp_path / "meta.txt", "w") as f:
+        f.write(f"{w.n_params} {w.dp} {rank} {w.steps}\n")
+        for e, r, c in w.shapes:
+            f.write(f"{e} {r} {c}\n")
+        f32 = [repr(float(np.float32(x))) for x in (hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
+                                                     hp.max_grad_norm)]  # exact float32 values
+        f.write(" ".join(f32) + "\n")
+        for t in range(w.steps):
+            f.write(f"{ref[rank][t]['extra']!r}\n")
+    for p in range(w.n_params):
+        P[p].tofile(tmp_path / f"master_{p}.bin")
+    for t in range(1, w.steps + 1):
+        G = harness.grads(w, t)
+        for p in range(w.n_params):
+            G[p].tofile(tmp_path / f"grad_{t}_{p}.bin")
+    env = {k: v for k, v in os.environ.items() if k != "PYTHONPATH"}
+    r = subprocess.run([exe, str(tmp_path)], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0, r.stderr
+    R = ref[rank][-1]
+    n = tabs[rank]["shard_slots"]
+    got = np.fromfile(tmp_path / "out_master.bin", dtype=np.float32).reshape(n, 128, 128)
+    assert got.tobytes() == R["master"].tobytes()
+    step, k, found, skipped = open(tmp_path / "out_state.txt").read().split()
+    assert int(step) == R["state"]["step"] and float(k) == R["state"]["k"]
+    mask = layout.valid_mask(tabs[rank])
+    held = {p: np.zeros(s, bool) for p, s in enumerate(w.shapes)}
+    layout.unfold_shard(tabs[rank], mask, held)
+    for p in range(w.n_params):
+        codes = np.fromfile(tmp_path / f"out_codes_{p}.bin", dtype=np.uint8).reshape(w.shapes[p])
+        assert (codes[held[p]] == un[-1]["codes"][p][held[p]]).all()
