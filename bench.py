@@ -42,7 +42,8 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 BLOCK = 128 * 128
 
-# Algorithmic bytes per real element (and per slot) of each call, see the design doc.
+# Algorithmic bytes per real element (and per slot) of each call: what each kernel
+# must read and write once (padding excluded), not what it happens to move.
 BYTES_FOLD_F32 = 8  # read 4, write 4
 BYTES_STATS = 4  # separate statistics kernel (not used when fused into the fold)
 BYTES_UPDATE = 29  # read g, p, m, v (16); write p, m, v (12) + code (1)
@@ -167,8 +168,8 @@ def main() -> int:
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic of the step kernels)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the multi-GPU path is a design, not a runnable configuration", file=sys.stderr)
+        print(f"bench.py: one GPU only (asked for --gpus {args.gpus}): the path runs one data-parallel rank's "
+              "shard; collectives across GPUs are not part of it", file=sys.stderr)
         return 2
 
     import torch
