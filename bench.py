@@ -49,7 +49,7 @@ BYTES_STATS = 4  # separate statistics kernel (not used when fused into the fold
 BYTES_UPDATE = 29  # read g, p, m, v (16); write p, m, v (12) + code (1)
 BYTES_UNFOLD_E4M3 = 2  # read code, write code
 SLOT_BYTES_UPDATE = 32 + 4  # slot plan record + scale
-SLOT_BYTES_FOLD = 32 + 8  # slot plan record + fused per-slot sum
+SLOT_BYTES_FOLD = 32 + 8  # slot plan record + the slot's float64 sum of squares
 SLOT_BYTES_UNFOLD = 32 + 8  # slot plan record + scale read and write
 
 

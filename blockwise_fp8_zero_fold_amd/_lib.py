@@ -19,6 +19,7 @@ lib_path = os.path.join(_HERE, "libfp8z1.so")
 F32, BF16, E4M3 = 0, 1, 2
 SCALE_AMAX, SCALE_POW2 = 0, 1
 SPLIT_BLOCK, SPLIT_PARAM = 0, 1
+STAT_PARTS = 4  # float64 partial sums of squares per slot
 ALL_RANKS = -1
 
 BLOCK_ENTRY_DTYPE = np.dtype([
@@ -235,7 +236,7 @@ def fp8z1_fold(table: Table, srcs: Sequence, src_dtype: int, dst, slot_sumsq=Non
     n = table.shard_slots
     _need(dst, n * 16384 * 4, "fold dst")
     if slot_sumsq is not None:
-        _need(slot_sumsq, n * 8, "fold slot_sumsq")
+        _need(slot_sumsq, n * STAT_PARTS * 8, "fold slot_sumsq")
     _check_param_list(table, srcs, src_dtype, "fold src")
     _check(lib.fp8z1_fold(table.handle, _ptr_list(srcs), src_dtype, _ptr(dst), _ptr(slot_sumsq), _stream(stream)),
            "fp8z1_fold")
@@ -263,7 +264,7 @@ def fp8z1_step(table: Table, hp: Hparams, d_state, grad, master, m, v, fp8, scal
     _need(scales, n * 4, "step scales")
     _need(d_state, 64, "step state")
     if workspace is not None:
-        _need(workspace, n * 8, "step workspace")
+        _need(workspace, n * STAT_PARTS * 8, "step workspace")
     _check(lib.fp8z1_step(table.handle, C.byref(hp), _ptr(d_state), _ptr(grad), _ptr(master), _ptr(m), _ptr(v),
                           _ptr(fp8), _ptr(scales), _ptr(workspace), workspace_bytes, int(bool(presummed)),
                           _stream(stream)), "fp8z1_step")
@@ -280,7 +281,7 @@ def fp8z1_step_rowmajor(table: Table, hp: Hparams, d_state, grads: Sequence, mas
     _need(scales, n * 4, "step_rowmajor scales")
     _need(d_state, 64, "step_rowmajor state")
     if workspace is not None:
-        _need(workspace, n * 8, "step_rowmajor workspace")
+        _need(workspace, n * STAT_PARTS * 8, "step_rowmajor workspace")
     _check_param_list(table, grads, F32, "step_rowmajor grads")
     _check(lib.fp8z1_step_rowmajor(table.handle, C.byref(hp), _ptr(d_state), _ptr_list(grads), _ptr(master), _ptr(m),
                                    _ptr(v), _ptr(fp8), _ptr(scales), _ptr(workspace), workspace_bytes,

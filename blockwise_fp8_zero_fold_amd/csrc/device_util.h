@@ -14,12 +14,21 @@ namespace fp8z1 {
 constexpr int kChunks = kBlockElems / 4;
 constexpr int kChunksPerRow = kB / 4;
 
-// Thread count and chunk order of the per-slot sum of squares.  The fold
-// (fused statistics) and the separate statistics kernel both use it, so the
-// two give bit-identical per-slot sums: thread t adds chunks t, t + 256, ...
-// in increasing order, the 4 elements of a chunk in increasing order, then
-// the block reduction below combines the 256 partial sums in a fixed order.
+// Work split of the kernels that read a slot row by row (fold, statistics):
+// a slot is kStatParts parts of kPartRows rows (one 16 KB float32 part per
+// workgroup, so the workgroups in flight cover a compact range), and the
+// grad statistics keep one float64 partial sum per part.  The fold (fused
+// statistics), the statistics pass over row-major grads and the statistics
+// kernel over folded grads all use this order, so they give bit-identical
+// partials: in part q, thread t adds the part's chunks t, t + 256, t + 512,
+// t + 768 in increasing order, the 4 elements of a chunk in increasing order,
+// then the block reduction below combines the 256 thread sums in a fixed order.
 constexpr int kSumThreads = 256;
+constexpr int kStatParts = FP8Z1_STAT_PARTS;
+static_assert(kB % kStatParts == 0 && (kChunks / kStatParts) % kSumThreads == 0, "part split");
+constexpr int kPartRows = kB / kStatParts;
+constexpr int kPartChunks = kChunks / kStatParts;
+constexpr int kPartPasses = kPartChunks / kSumThreads;
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

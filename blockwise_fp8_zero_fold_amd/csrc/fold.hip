@@ -6,10 +6,11 @@
 // swaps the block-column index with the row-within-block index, so each
 // 128-element row segment of the source moves whole to a contiguous 512-byte
 // destination.  The kernel is therefore a segment gather, not a transpose:
-// one workgroup per slot, 32 lanes per row segment, 16-byte loads (at any
-// element alignment of the source rows) and 16-byte stores; in a partial block
-// only the chunk across the last real column is loaded element by element.
-// Every source byte is read once, every destination byte written once.
+// four workgroups per slot (32 rows each), 32 lanes per row segment, 16-byte
+// loads (at any element alignment of the source rows) and 16-byte stores; in a
+// partial block only the chunk across the last real column is loaded element
+// by element.  Every source byte is read once, every destination byte
+// written once.
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"
@@ -18,7 +19,6 @@ namespace fp8z1 {
 namespace {
 
 constexpr int kFoldThreads = kSumThreads;  // also the statistics order
-constexpr int kPasses = kChunks / kFoldThreads;
 
 template <typename T>
 struct Src;
@@ -40,43 +40,47 @@ struct Src<uint16_t> {  // bfloat16 bits
   __device__ static float load1(const uint16_t* p) { return widen(*p); }
 };
 
-// WRITE = false: statistics only (the per-slot sums of a row-major grad that is
-// read by the update directly, without a folded copy).
+// One workgroup per part (kPartRows rows) of a slot.  SUMSQ: also write the
+// part's float64 sum of squares to part_sumsq[slot * kStatParts + part].
+// WRITE = false: statistics only (the partials of a row-major grad that the
+// update reads directly, without a folded copy).
 template <typename T, bool SUMSQ, bool WRITE = true>
 __global__ __launch_bounds__(kFoldThreads) void fold_kernel(const SlotPlan* __restrict__ plan,
                                                             const void* const* __restrict__ srcs,
                                                             float* __restrict__ dst,
-                                                            double* __restrict__ slot_sumsq) {
+                                                            double* __restrict__ part_sumsq) {
   __shared__ double red[kFoldThreads / 64];
-  const int64_t s = blockIdx.x;
+  const int64_t s = blockIdx.x / kStatParts;
+  const int part = blockIdx.x % kStatParts;
   const SlotPlan P = plan[s];
-  float4* out = WRITE ? reinterpret_cast<float4*>(dst + s * kBlockElems) : nullptr;
+  float4* out = WRITE ? reinterpret_cast<float4*>(dst + s * kBlockElems) + part * kPartChunks : nullptr;
   const int t = threadIdx.x;
   double acc = 0.0;
 
   if (P.param < 0) {
     if (WRITE) {
 #pragma unroll
-      for (int k = 0; k < kPasses; ++k) out[t + kFoldThreads * k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < kPartPasses; ++k) out[t + kFoldThreads * k] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
   } else {
     const T* src = static_cast<const T*>(srcs[P.param]) + P.off;
     const int64_t ld = P.ld;
     const int vr = P.vr, vc = P.vc;
-    float4 x[kPasses];
+    const int r0 = part * kPartRows;
+    float4 x[kPartPasses];
     if (vr == kB && vc == kB) {
 #pragma unroll
-      for (int k = 0; k < kPasses; ++k) {
+      for (int k = 0; k < kPartPasses; ++k) {
         const int c = t + kFoldThreads * k;
-        x[k] = Src<T>::load4(src + (c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow));
+        x[k] = Src<T>::load4(src + (r0 + c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow));
       }
     } else {
       // partial block: whole chunks inside the real region load as vectors, the
       // chunk across the last real column element by element, the rest is padding
 #pragma unroll
-      for (int k = 0; k < kPasses; ++k) {
+      for (int k = 0; k < kPartPasses; ++k) {
         const int c = t + kFoldThreads * k;
-        const int i = c / kChunksPerRow, j = 4 * (c % kChunksPerRow);
+        const int i = r0 + c / kChunksPerRow, j = 4 * (c % kChunksPerRow);
         const T* row = src + i * ld + j;
         if (i < vr && j + 4 <= vc) {
           x[k] = Src<T>::load4(row);
@@ -90,7 +94,7 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(const SlotPlan* __re
       }
     }
 #pragma unroll
-    for (int k = 0; k < kPasses; ++k) {
+    for (int k = 0; k < kPartPasses; ++k) {
       if (WRITE) out[t + kFoldThreads * k] = x[k];
       if (SUMSQ) {
         // padding positions hold +0 and add nothing
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(const SlotPlan* __re
   }
   if (SUMSQ) {
     const double tot = block_sum<kFoldThreads>(acc, red);
-    if (t == 0) slot_sumsq[s] = tot;
+    if (t == 0) part_sumsq[s * kStatParts + part] = tot;
   }
 }
 
@@ -111,11 +115,11 @@ template <typename T>
 hipError_t launch(const SlotPlan* plan, void** srcs, float* dst, double* sumsq, int64_t nslots,
                   hipStream_t stream) {
   if (nslots == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(nslots * kStatParts));
   if (sumsq)
-    hipLaunchKernelGGL((fold_kernel<T, true>), dim3(nslots), dim3(kFoldThreads), 0, stream, plan, srcs, dst, sumsq);
+    hipLaunchKernelGGL((fold_kernel<T, true>), grid, dim3(kFoldThreads), 0, stream, plan, srcs, dst, sumsq);
   else
-    hipLaunchKernelGGL((fold_kernel<T, false>), dim3(nslots), dim3(kFoldThreads), 0, stream, plan, srcs, dst,
-                       sumsq);
+    hipLaunchKernelGGL((fold_kernel<T, false>), grid, dim3(kFoldThreads), 0, stream, plan, srcs, dst, sumsq);
   return hipGetLastError();
 }
 
@@ -123,8 +127,8 @@ hipError_t launch(const SlotPlan* plan, void** srcs, float* dst, double* sumsq, 
 
 hipError_t launch_grad_sumsq(const SlotPlan* plan, void** grads, double* sumsq, int64_t nslots, hipStream_t stream) {
   if (nslots == 0) return hipSuccess;
-  hipLaunchKernelGGL((fold_kernel<float, true, false>), dim3(nslots), dim3(kFoldThreads), 0, stream, plan, grads,
-                     nullptr, sumsq);
+  hipLaunchKernelGGL((fold_kernel<float, true, false>), dim3(static_cast<unsigned>(nslots * kStatParts)),
+                     dim3(kFoldThreads), 0, stream, plan, grads, nullptr, sumsq);
   return hipGetLastError();
 }
 
@@ -150,6 +154,7 @@ extern "C" int fp8z1_fold(const fp8z1_table* ct, const void* const* src, int32_t
   if (reinterpret_cast<uintptr_t>(dst) % 16) return set_error(FP8Z1_EINVAL, "fold: dst must be 16-byte aligned");
   if (slot_sumsq && reinterpret_cast<uintptr_t>(slot_sumsq) % 8)
     return set_error(FP8Z1_EINVAL, "fold: slot_sumsq must be 8-byte aligned");
+  if (t->info.shard_slots * kStatParts > 0x7fffffffLL) return set_error(FP8Z1_ESHAPE, "fold: too many slots");
   std::lock_guard<std::mutex> lock(t->mu);
   int rc = ensure_device(t);
   if (rc) return rc;

@@ -9,9 +9,9 @@
 // overflow = inf/NaN in the grads, which skips the step (section 9, Q6).
 //
 // Kernels, all on the caller's stream, no host synchronization:
-//   K1 sumsq_kernel   one workgroup per slot: float64 sum of squares of the
-//                     slot's real grads -> workspace[slot]   (level 1)
-//   K2 finalize_kernel one workgroup: fixed-order float64 sum of the slot
+//   K1 sumsq_kernel   one workgroup per quarter slot: float64 sum of squares
+//                     of its real grads -> workspace[4 * slot + part] (level 1)
+//   K2 finalize_kernel one workgroup: fixed-order float64 sum of the part
 //                     sums + the other ranks' sum -> overflow flag, clip and
 //                     unscale factor k, bias-correction scalars, loss scale;
 //                     written to the device state                (level 2)
@@ -33,20 +33,23 @@ namespace {
 
 // ---------------------------------------------------------------- K1
 
+// one workgroup per part of a slot, the order of the fold's fused statistics
 __global__ __launch_bounds__(kSumThreads) void sumsq_kernel(const SlotPlan* __restrict__ plan,
                                                             const float* __restrict__ grad,
                                                             double* __restrict__ out) {
   __shared__ double red[kSumThreads / 64];
-  const int64_t s = blockIdx.x;
+  const int64_t s = blockIdx.x / kStatParts;
+  const int part = blockIdx.x % kStatParts;
   const SlotPlan P = plan[s];
   const int t = threadIdx.x;
   double acc = 0.0;
   if (P.param >= 0) {
-    const float4* g = reinterpret_cast<const float4*>(grad + s * kBlockElems);
+    const float4* g = reinterpret_cast<const float4*>(grad + s * kBlockElems) + part * kPartChunks;
     const int vr = P.vr, vc = P.vc;
+    const int r0 = part * kPartRows;
     if (vr == kB && vc == kB) {
 #pragma unroll
-      for (int k = 0; k < kChunks / kSumThreads; ++k) {
+      for (int k = 0; k < kPartPasses; ++k) {
         const float4 x = g[t + kSumThreads * k];
         acc += sq64(x.x);
         acc += sq64(x.y);
@@ -55,9 +58,9 @@ __global__ __launch_bounds__(kSumThreads) void sumsq_kernel(const SlotPlan* __re
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < kChunks / kSumThreads; ++k) {
+      for (int k = 0; k < kPartPasses; ++k) {
         const int c = t + kSumThreads * k;
-        const int i = c / kChunksPerRow, j = 4 * (c % kChunksPerRow);
+        const int i = r0 + c / kChunksPerRow, j = 4 * (c % kChunksPerRow);
         if (i < vr && j < vc) {
           const float4 x = g[c];
           // masked positions add +0, exactly what the fold's zero padding adds
@@ -75,7 +78,7 @@ __global__ __launch_bounds__(kSumThreads) void sumsq_kernel(const SlotPlan* __re
     }
   }
   const double tot = block_sum<kSumThreads>(acc, red);
-  if (t == 0) out[s] = tot;
+  if (t == 0) out[s * kStatParts + part] = tot;
 }
 
 // ---------------------------------------------------------------- K2
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(const double* __r
   __shared__ double red[kFinThreads / 64];
   double acc = 0.0;
   if (a.have_stats)
-    for (int64_t i = threadIdx.x; i < a.nslots; i += kFinThreads) acc += partial[i];
+    for (int64_t i = threadIdx.x; i < a.nslots * kStatParts; i += kFinThreads) acc += partial[i];
   const double local = block_sum<kFinThreads>(acc, red);
   if (threadIdx.x != 0) return;
 
@@ -377,7 +380,7 @@ extern "C" int fp8z1_state_init(const fp8z1_hparams* hp, fp8z1_state* d_state, v
 
 extern "C" int fp8z1_step_workspace_bytes(const fp8z1_table* t, size_t* bytes) {
   if (!t || !bytes) return set_error(FP8Z1_EINVAL, "step_workspace_bytes: NULL argument");
-  *bytes = static_cast<size_t>(t->info.shard_slots) * sizeof(double);
+  *bytes = static_cast<size_t>(t->info.shard_slots) * kStatParts * sizeof(double);
   return FP8Z1_OK;
 }
 
@@ -412,9 +415,10 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
   }
   const bool stats = hp->max_grad_norm > 0.0f || hp->loss_scaling != 0;
   const int64_t n = t->info.shard_slots;
+  if (n * kStatParts > 0x7fffffffLL) return set_error(FP8Z1_ESHAPE, std::string(who) + ": too many slots");
   if (stats) {
     if (!d_workspace) return set_error(FP8Z1_EINVAL, std::string(who) + ": statistics need the workspace");
-    if (workspace_bytes < static_cast<size_t>(n) * sizeof(double))
+    if (workspace_bytes < static_cast<size_t>(n) * kStatParts * sizeof(double))
       return set_error(FP8Z1_EINVAL, std::string(who) + ": workspace smaller than fp8z1_step_workspace_bytes()");
     if (reinterpret_cast<uintptr_t>(d_workspace) % 8)
       return set_error(FP8Z1_EINVAL, std::string(who) + ": misaligned workspace");
@@ -433,7 +437,8 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
     if (grad_rows)
       rc = check_hip(launch_grad_sumsq(t->d_plan, drows, partial, n, s), "step: statistics launch");
     else {
-      hipLaunchKernelGGL(sumsq_kernel, dim3(n), dim3(kSumThreads), 0, s, t->d_plan, grad, partial);
+      hipLaunchKernelGGL(sumsq_kernel, dim3(static_cast<unsigned>(n * kStatParts)), dim3(kSumThreads), 0, s,
+                         t->d_plan, grad, partial);
       rc = check_hip(hipGetLastError(), "step: statistics launch");
     }
     if (rc) return rc;

@@ -31,7 +31,7 @@ class Shard:
         self.v = torch.zeros(n * BLOCK_ELEMS, **f32)
         self.fp8 = torch.zeros(n * BLOCK_ELEMS, dtype=torch.uint8, device=dev)
         self.scales = torch.zeros(max(n, 1), **f32)
-        self.workspace = torch.zeros(max(n, 1), dtype=torch.float64, device=dev)
+        self.workspace = torch.zeros(max(n * L.STAT_PARTS, 1), dtype=torch.float64, device=dev)
         self.state = torch.zeros(8, dtype=torch.float64, device=dev)  # 64 bytes
 
     def held_params(self):
@@ -48,7 +48,7 @@ class Shard:
     def fold_grads(self, hp: L.Hparams, grads: Sequence[Optional[torch.Tensor]], fused_stats: bool = True,
                    stream=None) -> bool:
         """Fold the reduced row-major FP32 grads; with fused_stats (and statistics on) the
-        fold also writes the per-slot sums of squares.  Returns whether it did."""
+        fold also writes the per-part sums of squares.  Returns whether it did."""
         stats = hp.max_grad_norm > 0 or hp.loss_scaling
         pre = bool(fused_stats and stats)
         L.fp8z1_fold(self.table, grads, L.F32, self.grad, slot_sumsq=self.workspace if pre else None,

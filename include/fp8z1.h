@@ -70,6 +70,7 @@ extern "C" {
 #define FP8Z1_E4M3 2 /* OCP FP8 E4M3 codes, one byte each */
 
 #define FP8Z1_BLOCK 128 /* block edge */
+#define FP8Z1_STAT_PARTS 4 /* float64 partial sums of squares per slot (one per 32 rows) */
 
 /* block scale rules */
 #define FP8Z1_SCALE_AMAX 0 /* scale = amax / 448 in float32 (1 if amax = 0) */
@@ -166,9 +167,10 @@ void fp8z1_table_free(fp8z1_table* table);
  * an entry may be NULL if the shard holds no block of that param.  Padding
  * positions and padding slots are written +0.  Used on the FP32/BF16
  * weights at init and on the reduced FP32 grads every step.
- * If slot_sumsq is not NULL (device, shard_slots doubles), each slot's sum of
- * squares of its real elements (in float64, in a fixed order) is written
- * there as well, in the form fp8z1_step takes as its statistics. */
+ * If slot_sumsq is not NULL (device, 4*shard_slots doubles, 8-byte aligned),
+ * the float64 sum of squares of the real elements of each quarter of each
+ * slot (rows 32q..32q+31 of slot s at index 4s+q, in a fixed order) is
+ * written there as well, in the form fp8z1_step takes as its statistics. */
 int fp8z1_fold(const fp8z1_table* table, const void* const* src, int32_t src_dtype, float* dst, double* slot_sumsq,
                void* stream);
 
@@ -176,8 +178,8 @@ int fp8z1_fold(const fp8z1_table* table, const void* const* src, int32_t src_dty
  * (device, 64 bytes). */
 int fp8z1_state_init(const fp8z1_hparams* hp, fp8z1_state* d_state, void* stream);
 
-/* Bytes of device workspace fp8z1_step needs (the per-slot float64 partial
- * sums of squares: 8 bytes per slot). */
+/* Bytes of device workspace fp8z1_step needs (the float64 partial sums of
+ * squares, one per quarter slot: 32 bytes per slot). */
 int fp8z1_step_workspace_bytes(const fp8z1_table* table, size_t* bytes);
 
 /* One optimizer step on the shard (section "总结"; step order of
@@ -187,7 +189,7 @@ int fp8z1_step_workspace_bytes(const fp8z1_table* table, size_t* bytes);
  *  1. statistics (only if hp->max_grad_norm > 0 or hp->loss_scaling): the
  *     float64 sum of squares of the shard's real grads, plus hp->extra_sumsq;
  *     overflow if that sum is not finite or hp->extra_found_inf is set.
- *     If `presummed` is nonzero, d_workspace already holds per-slot sums
+ *     If `presummed` is nonzero, d_workspace already holds the partial sums
  *     from fp8z1_fold(slot_sumsq = d_workspace) of this same grad and the
  *     grad is not read for them again.
  *  2. on overflow: skip (master, m, v, fp8, scales untouched), S *= backoff.
@@ -213,7 +215,7 @@ int fp8z1_step(const fp8z1_table* table, const fp8z1_hparams* hp, fp8z1_state* d
  * update, and no folded copy of the grads is written.  grads: host array of
  * n_params device pointers to row-major FP32 [E,R,C] grads, 4-byte aligned
  * (NULL allowed for params the shard holds no block of).  With statistics
- * on, a first pass over the same grads writes the per-slot sums of squares
+ * on, a first pass over the same grads writes the partial sums of squares
  * into d_workspace, in the order fp8z1_fold uses.  Results (state, master,
  * m, v, fp8, scales) are bit-identical to fp8z1_fold followed by
  * fp8z1_step. */

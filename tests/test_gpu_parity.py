@@ -134,12 +134,23 @@ def test_fused_statistics_equal_separate_kernel(name):
         sh.fold_grads(hp, g, fused_stats=True)
         fused = sh.workspace.cpu().numpy().copy()
         sh.update(hp, presummed=False)  # recomputes the sums with the statistics kernel
-        sep = sh.workspace.cpu().numpy()
+        sep = sh.workspace.cpu().numpy().copy()
         assert fused.tobytes() == sep.tobytes()
+        sh.workspace.fill_(-1.0)
+        sh.update_rowmajor(hp, g)  # the statistics pass over the row-major grads
+        rowmajor = sh.workspace.cpu().numpy()
+        assert fused.tobytes() == rowmajor.tobytes()
         gf = layout.fold_shard(tab, harness.grads(w, 1))
         mask = layout.valid_mask(tab)
-        want = np.array([optim.local_sumsq(gf[s][mask[s]]) for s in range(len(mask))])
-        assert np.all(np.abs(fused[:len(want)] - want) <= 1e-12 * np.abs(want))
+        n = len(mask)
+        parts = fused[:n * fz.STAT_PARTS].reshape(n, fz.STAT_PARTS)
+        rows = 128 // fz.STAT_PARTS
+        for q in range(fz.STAT_PARTS):
+            sl = slice(rows * q, rows * (q + 1))
+            want_q = np.array([optim.local_sumsq(gf[s][sl][mask[s][sl]]) for s in range(n)])
+            assert np.all(np.abs(parts[:, q] - want_q) <= 1e-12 * np.abs(want_q)), q
+        want = np.array([optim.local_sumsq(gf[s][mask[s]]) for s in range(n)])
+        assert np.all(np.abs(parts.sum(axis=1) - want) <= 1e-12 * np.abs(want))
 
 
 # ---------------------------------------------------------------- the step

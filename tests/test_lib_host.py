@@ -129,3 +129,16 @@ def test_argument_errors_before_any_gpu_work():
     with pytest.raises(fz.Fp8z1Error, match="NULL"):
         fz.fp8z1_unfold(t, 16, fz.E4M3, None, [None], stream=0)
     t.free()
+
+
+def test_workspace_bytes_and_constants_match_header():
+    text = "".join(open(h).read() for h in HEADERS)
+    defs = dict(re.findall(r"#define (FP8Z1_[A-Z0-9_]+) \(?(-?\d+)\)?", text))
+    for name, val in (("F32", fz.F32), ("BF16", fz.BF16), ("E4M3", fz.E4M3), ("SCALE_AMAX", fz.SCALE_AMAX),
+                      ("SCALE_POW2", fz.SCALE_POW2), ("SPLIT_BLOCK", fz.SPLIT_BLOCK), ("SPLIT_PARAM", fz.SPLIT_PARAM),
+                      ("ALL_RANKS", fz.ALL_RANKS), ("STAT_PARTS", fz.STAT_PARTS)):
+        assert int(defs["FP8Z1_" + name]) == val, name
+    for name in ("tiny", "ragged_small"):
+        w = synth.get(name)
+        t = fz.fp8z1_build_table(w.shapes, w.dp, 0, 0)
+        assert fz.fp8z1_step_workspace_bytes(t) == 8 * fz.STAT_PARTS * t.shard_slots
