@@ -149,6 +149,27 @@ def cpu_baseline(w, rank: int, slots: int, steps: int = 2):
     return valid / dt, valid, dt
 
 
+def _device_info() -> dict:
+    """What identifies the GPU and its memory set-up (bandwidth differs between parts)."""
+    import glob
+
+    import torch
+    pr = torch.cuda.get_device_properties(0)
+    info = {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "cus": pr.multi_processor_count,
+            "hbm_gib": round(pr.total_memory / 2**30, 1), "l2_bytes": getattr(pr, "L2_cache_size", None)}
+    uuid = getattr(pr, "uuid", None)
+    if uuid is not None:
+        info["uuid"] = str(uuid)
+    for key in ("current_memory_partition", "current_compute_partition"):
+        for f in sorted(glob.glob(f"/sys/class/drm/card*/device/{key}")):
+            try:
+                info[key] = open(f).read().strip()
+                break
+            except OSError:
+                pass
+    return info
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -368,6 +389,7 @@ def main() -> int:
         "alt_mode": {"mode": alt_mode, "ms_per_step": alt_ms, "value": valid / (alt_ms * 1e-3),
                      "per_call_ms": alt_calls, "gbs_algorithmic": alt_total / (alt_ms * 1e-3) / 1e9},
         "cpu_baseline": cpu,
+        "device": _device_info(),
         "source_hash": src_hash,
     }
     print(json.dumps(out), flush=True)

@@ -56,14 +56,20 @@ class Hparams(C.Structure):
                 ("weight_decay", C.c_float), ("max_grad_norm", C.c_float), ("loss_scaling", C.c_int32),
                 ("init_scale", C.c_float), ("growth_factor", C.c_float), ("backoff_factor", C.c_float),
                 ("growth_interval", C.c_int32), ("extra_found_inf", C.c_int32), ("scale_rule", C.c_int32),
-                ("extra_sumsq", C.c_double)]
+                ("extra_sumsq", C.c_double), ("d_global_sumsq", C.c_void_p)]
 
     @classmethod
-    def make(cls, hp, extra_sumsq: float = 0.0, extra_found_inf: bool = False) -> "Hparams":
-        """From any object with the same attribute names (e.g. synth.Hparams)."""
-        return cls(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.max_grad_norm, int(bool(hp.loss_scaling)),
-                   hp.init_scale, hp.growth_factor, hp.backoff_factor, int(hp.growth_interval),
-                   int(bool(extra_found_inf)), int(getattr(hp, "scale_rule", 0)), float(extra_sumsq))
+    def make(cls, hp, extra_sumsq: float = 0.0, extra_found_inf: bool = False, global_sumsq=None) -> "Hparams":
+        """From any object with the same attribute names (e.g. synth.Hparams).  global_sumsq:
+        None, or a device float64 tensor (or address) holding the all-ranks sum of squares."""
+        if global_sumsq is not None and not isinstance(global_sumsq, int):
+            _need(global_sumsq, 8, "global_sumsq", torch.float64)
+        out = cls(hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, hp.max_grad_norm, int(bool(hp.loss_scaling)),
+                  hp.init_scale, hp.growth_factor, hp.backoff_factor, int(hp.growth_interval),
+                  int(bool(extra_found_inf)), int(getattr(hp, "scale_rule", 0)), float(extra_sumsq),
+                  _ptr(global_sumsq))
+        out._keep = global_sumsq  # the tensor must outlive the calls that use these settings
+        return out
 
 
 class State(C.Structure):
@@ -76,7 +82,7 @@ class State(C.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
-assert C.sizeof(Block) == 16 and C.sizeof(State) == 64 and C.sizeof(Hparams) == 64
+assert C.sizeof(Block) == 16 and C.sizeof(State) == 64 and C.sizeof(Hparams) == 72
 
 _vp = C.c_void_p
 _sig = {
@@ -89,6 +95,7 @@ _sig = {
     "fp8z1_fold": (C.c_int, [_vp, C.POINTER(_vp), C.c_int32, _vp, _vp, _vp]),
     "fp8z1_state_init": (C.c_int, [C.POINTER(Hparams), _vp, _vp]),
     "fp8z1_step_workspace_bytes": (C.c_int, [_vp, C.POINTER(C.c_size_t)]),
+    "fp8z1_shard_sumsq": (C.c_int, [_vp, _vp, _vp, _vp]),
     "fp8z1_step": (C.c_int, [_vp, C.POINTER(Hparams), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, C.c_size_t, C.c_int32,
                              _vp]),
     "fp8z1_step_rowmajor": (C.c_int, [_vp, C.POINTER(Hparams), _vp, C.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, _vp,
@@ -233,8 +240,10 @@ def _check_param_list(table: Table, xs: Sequence, dtype: int, what: str, scales:
 
 
 def fp8z1_fold(table: Table, srcs: Sequence, src_dtype: int, dst, slot_sumsq=None, stream=None) -> None:
+    """dst None with slot_sumsq given: the statistics pass alone (row-major FP32 grads)."""
     n = table.shard_slots
-    _need(dst, n * 16384 * 4, "fold dst")
+    if dst is not None:
+        _need(dst, n * 16384 * 4, "fold dst")
     if slot_sumsq is not None:
         _need(slot_sumsq, n * STAT_PARTS * 8, "fold slot_sumsq")
     _check_param_list(table, srcs, src_dtype, "fold src")
@@ -251,6 +260,13 @@ def fp8z1_step_workspace_bytes(table: Table) -> int:
     n = C.c_size_t()
     _check(lib.fp8z1_step_workspace_bytes(table.handle, C.byref(n)), "fp8z1_step_workspace_bytes")
     return n.value
+
+
+def fp8z1_shard_sumsq(table: Table, partials, out, stream=None) -> None:
+    """Sum the shard's partial sums of squares (as fp8z1_fold wrote them) into out[0] (float64)."""
+    _need(partials, table.shard_slots * STAT_PARTS * 8, "shard_sumsq partials", torch.float64)
+    _need(out, 8, "shard_sumsq out", torch.float64)
+    _check(lib.fp8z1_shard_sumsq(table.handle, _ptr(partials), _ptr(out), _stream(stream)), "fp8z1_shard_sumsq")
 
 
 def fp8z1_step(table: Table, hp: Hparams, d_state, grad, master, m, v, fp8, scales, workspace=None,

@@ -139,9 +139,11 @@ using namespace fp8z1;
 extern "C" int fp8z1_fold(const fp8z1_table* ct, const void* const* src, int32_t src_dtype, float* dst,
                           double* slot_sumsq, void* stream) {
   fp8z1_table* t = const_cast<fp8z1_table*>(ct);
-  if (!t || !src || !dst) return set_error(FP8Z1_EINVAL, "fold: NULL table, src list or dst");
+  if (!t || !src || !(dst || slot_sumsq)) return set_error(FP8Z1_EINVAL, "fold: NULL table, src list or dst");
   if (src_dtype != FP8Z1_F32 && src_dtype != FP8Z1_BF16)
     return set_error(FP8Z1_EINVAL, "fold: src_dtype must be FP8Z1_F32 or FP8Z1_BF16");
+  if (!dst && src_dtype != FP8Z1_F32)
+    return set_error(FP8Z1_EINVAL, "fold: the statistics-only pass (dst NULL) takes FP8Z1_F32 grads");
   const size_t el = src_dtype == FP8Z1_F32 ? 4 : 2;
   // every param the shard holds needs a source pointer, element-aligned
   for (const fp8z1_block& e : t->entries) {
@@ -156,12 +158,13 @@ extern "C" int fp8z1_fold(const fp8z1_table* ct, const void* const* src, int32_t
     return set_error(FP8Z1_EINVAL, "fold: slot_sumsq must be 8-byte aligned");
   if (t->info.shard_slots * kStatParts > 0x7fffffffLL) return set_error(FP8Z1_ESHAPE, "fold: too many slots");
   std::lock_guard<std::mutex> lock(t->mu);
-  int rc = ensure_device(t);
+  int rc = ensure_device(t, stream);
   if (rc) return rc;
   void** dsrc = nullptr;
   rc = device_ptr_list(t, kRoleFoldSrc, src, &dsrc, stream);
   if (rc) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!dst) return check_hip(launch_grad_sumsq(t->d_plan, dsrc, slot_sumsq, t->info.shard_slots, st), "fold: launch");
   hipError_t e = src_dtype == FP8Z1_F32
                      ? launch<float>(t->d_plan, dsrc, dst, slot_sumsq, t->info.shard_slots, st)
                      : launch<uint16_t>(t->d_plan, dsrc, dst, slot_sumsq, t->info.shard_slots, st);

@@ -55,9 +55,11 @@ struct fp8z1_table {
 namespace fp8z1 {
 
 int set_error(int status, const std::string& msg);
-// Bind the table to the current device and upload its plan (first call only).
-int ensure_device(fp8z1_table* t);
-// Upload (if changed) a host list of n_params device pointers; returns the device array.
+// Bind the table to the current device and upload its plan (first call only;
+// refused while `stream` is being captured).
+int ensure_device(fp8z1_table* t, void* stream);
+// Upload (if changed) a host list of n_params device pointers; returns the device
+// array.  A change is refused while `stream` is being captured.
 int device_ptr_list(fp8z1_table* t, PtrRole role, const void* const* host_list, void*** out, void* stream);
 int check_hip(int hip_status, const char* what);
 

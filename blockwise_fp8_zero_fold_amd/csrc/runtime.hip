@@ -14,7 +14,20 @@ int check_hip(int hip_status, const char* what) {
   return set_error(FP8Z1_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-int ensure_device(fp8z1_table* t) {
+// The set-up below allocates, copies synchronously and waits on events, none
+// of which may happen while `stream` is being captured into a graph; the
+// callers ask this only on those slow paths, so a captured call costs nothing.
+static int refuse_in_capture(void* stream, const char* what) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  int rc = check_hip(hipStreamIsCapturing(static_cast<hipStream_t>(stream), &st), "hipStreamIsCapturing");
+  if (rc) return rc;
+  if (st != hipStreamCaptureStatusNone)
+    return set_error(FP8Z1_EINVAL, std::string(what) +
+                                       " inside a stream capture: make the same call once outside the capture first");
+  return FP8Z1_OK;
+}
+
+int ensure_device(fp8z1_table* t, void* stream) {
   int dev = -1;
   int rc = check_hip(hipGetDevice(&dev), "hipGetDevice");
   if (rc) return rc;
@@ -24,6 +37,8 @@ int ensure_device(fp8z1_table* t) {
                                            std::to_string(dev));
     return FP8Z1_OK;
   }
+  rc = refuse_in_capture(stream, "first device use of a table");
+  if (rc) return rc;
   const size_t n = t->entries.size();
   std::vector<SlotPlan> plan(n);
   for (size_t s = 0; s < n; ++s) {
@@ -68,15 +83,17 @@ int device_ptr_list(fp8z1_table* t, PtrRole role, const void* const* host_list, 
   PtrCache& c = t->ptrs[role];
   const size_t bytes = sizeof(void*) * t->shapes.size();
   if (!c.valid || std::memcmp(c.host, host_list, bytes) != 0) {
+    int rc = refuse_in_capture(stream, "new param pointers");
+    if (rc) return rc;
     hipEvent_t ev = static_cast<hipEvent_t>(c.done);
     if (c.valid) {
       // the previous upload may still be reading the pinned mirror
-      int rc = check_hip(hipEventSynchronize(ev), "hipEventSynchronize");
+      rc = check_hip(hipEventSynchronize(ev), "hipEventSynchronize");
       if (rc) return rc;
     }
     std::memcpy(c.host, host_list, bytes);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    int rc = check_hip(hipMemcpyAsync(c.dev, c.host, bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync(pointer list)");
+    rc = check_hip(hipMemcpyAsync(c.dev, c.host, bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync(pointer list)");
     if (!rc) rc = check_hip(hipEventRecord(ev, s), "hipEventRecord");
     if (rc) {
       c.valid = false;

@@ -85,6 +85,7 @@ __global__ __launch_bounds__(kSumThreads) void sumsq_kernel(const SlotPlan* __re
 
 struct FinalizeArgs {
   double extra_sumsq;
+  const double* global_sumsq;  // device; when set, the global sum itself (partials unused)
   int64_t nslots;
   float lr, beta1, beta2, weight_decay, max_grad_norm;
   float growth_factor, backoff_factor;
@@ -96,13 +97,27 @@ struct FinalizeArgs {
 
 constexpr int kFinThreads = 256;
 
+// Level 2 of the sum of squares: the shard's partials (one per quarter slot)
+// summed in a fixed order -- lane i takes partials i, i + 256, ... in
+// increasing order, then the block reduction.  Every lane gets the total.
+__device__ __forceinline__ double sum_partials(const double* __restrict__ partial, int64_t count, double* red) {
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < count; i += kFinThreads) acc += partial[i];
+  return block_sum<kFinThreads>(acc, red);
+}
+
+__global__ __launch_bounds__(kFinThreads) void shard_sumsq_kernel(const double* __restrict__ partial, int64_t count,
+                                                                  double* __restrict__ out) {
+  __shared__ double red[kFinThreads / 64];
+  const double tot = sum_partials(partial, count, red);
+  if (threadIdx.x == 0) *out = tot;
+}
+
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(const double* __restrict__ partial,
                                                                fp8z1_state* __restrict__ st, FinalizeArgs a) {
   __shared__ double red[kFinThreads / 64];
-  double acc = 0.0;
-  if (a.have_stats)
-    for (int64_t i = threadIdx.x; i < a.nslots * kStatParts; i += kFinThreads) acc += partial[i];
-  const double local = block_sum<kFinThreads>(acc, red);
+  const bool own = a.have_stats && !a.global_sumsq;  // uniform over the workgroup
+  const double local = own ? sum_partials(partial, a.nslots * kStatParts, red) : 0.0;
   if (threadIdx.x != 0) return;
 
   fp8z1_state S = *st;
@@ -110,7 +125,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(const double* __r
   double glob = 0.0;
   bool found = false;
   if (a.have_stats) {
-    glob = local + a.extra_sumsq;
+    glob = a.global_sumsq ? *a.global_sumsq : local + a.extra_sumsq;
     found = !isfinite(glob) || a.extra_found_inf != 0;
   }
   S.global_sumsq = glob;
@@ -384,6 +399,17 @@ extern "C" int fp8z1_step_workspace_bytes(const fp8z1_table* t, size_t* bytes) {
   return FP8Z1_OK;
 }
 
+extern "C" int fp8z1_shard_sumsq(const fp8z1_table* t, const double* d_partials, double* d_sum, void* stream) {
+  if (!t || !d_sum || (!d_partials && t->info.shard_slots > 0))
+    return set_error(FP8Z1_EINVAL, "shard_sumsq: NULL argument");
+  if (reinterpret_cast<uintptr_t>(d_partials) % 8 || reinterpret_cast<uintptr_t>(d_sum) % 8)
+    return set_error(FP8Z1_EINVAL, "shard_sumsq: partials and sum must be 8-byte aligned");
+  const int64_t count = t->info.shard_slots * kStatParts;
+  hipLaunchKernelGGL(shard_sumsq_kernel, dim3(1), dim3(kFinThreads), 0, static_cast<hipStream_t>(stream), d_partials,
+                     count, d_sum);
+  return check_hip(hipGetLastError(), "shard_sumsq: launch");
+}
+
 namespace {
 
 int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, const float* grad,
@@ -414,9 +440,12 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
     }
   }
   const bool stats = hp->max_grad_norm > 0.0f || hp->loss_scaling != 0;
+  const bool given = stats && hp->d_global_sumsq != nullptr;  // global sum from the caller, on the device
   const int64_t n = t->info.shard_slots;
   if (n * kStatParts > 0x7fffffffLL) return set_error(FP8Z1_ESHAPE, std::string(who) + ": too many slots");
-  if (stats) {
+  if (given && reinterpret_cast<uintptr_t>(hp->d_global_sumsq) % 8)
+    return set_error(FP8Z1_EINVAL, std::string(who) + ": misaligned d_global_sumsq");
+  if (stats && !given) {
     if (!d_workspace) return set_error(FP8Z1_EINVAL, std::string(who) + ": statistics need the workspace");
     if (workspace_bytes < static_cast<size_t>(n) * kStatParts * sizeof(double))
       return set_error(FP8Z1_EINVAL, std::string(who) + ": workspace smaller than fp8z1_step_workspace_bytes()");
@@ -424,7 +453,7 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
       return set_error(FP8Z1_EINVAL, std::string(who) + ": misaligned workspace");
   }
   std::lock_guard<std::mutex> lock(t->mu);
-  int rc = ensure_device(t);
+  int rc = ensure_device(t, stream);
   if (rc) return rc;
   void** drows = nullptr;
   if (grad_rows) {
@@ -433,7 +462,7 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   double* partial = static_cast<double*>(d_workspace);
-  if (stats && !presummed && n > 0) {
+  if (stats && !given && !presummed && n > 0) {
     if (grad_rows)
       rc = check_hip(launch_grad_sumsq(t->d_plan, drows, partial, n, s), "step: statistics launch");
     else {
@@ -445,6 +474,7 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
   }
   FinalizeArgs fa;
   fa.extra_sumsq = hp->extra_sumsq;
+  fa.global_sumsq = given ? hp->d_global_sumsq : nullptr;
   fa.nslots = n;
   fa.lr = hp->lr;
   fa.beta1 = hp->beta1;

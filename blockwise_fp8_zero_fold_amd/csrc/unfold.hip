@@ -111,7 +111,7 @@ extern "C" int fp8z1_unfold(const fp8z1_table* ct, const void* folded, int32_t d
       return set_error(FP8Z1_EINVAL, "unfold: scale pointer of param " + std::to_string(e.param) + " is NULL or misaligned");
   }
   std::lock_guard<std::mutex> lock(t->mu);
-  int rc = ensure_device(t);
+  int rc = ensure_device(t, stream);
   if (rc) return rc;
   void** ddst = nullptr;
   rc = device_ptr_list(t, kRoleUnfoldDst, const_cast<const void* const*>(dst), &ddst, stream);

@@ -34,6 +34,17 @@
  *     calls that use one table must be issued on one stream, or ordered by
  *     the caller; calls on distinct tables are independent and thread-safe.
  *     fp8z1_table_free waits for the device to finish before releasing.
+ *   - Graph capture: fp8z1_fold, fp8z1_step, fp8z1_step_rowmajor,
+ *     fp8z1_unfold, fp8z1_state_init and fp8z1_dequantize only launch
+ *     kernels once a table is set up on the device and its pointer lists
+ *     are current, so they may be captured into a HIP graph after the same
+ *     call (same table, same param pointer arrays) has run once outside the
+ *     capture.  A captured call that would need set-up (first device use of
+ *     the table, or param pointers that differ from the last call of the
+ *     same kind) returns FP8Z1_EINVAL instead.  A replayed graph reads the
+ *     table's current pointer lists: a later uncaptured call with other
+ *     param pointers retargets it, so keep them fixed while the graph is in
+ *     use.  fp8z1_state_read/state_write synchronize and cannot be captured.
  *   - Rows of row-major arrays may start at any element alignment: kernels
  *     use 16-byte accesses (gfx950 runs in unaligned-access mode) but never
  *     touch a byte outside the block row segment they own.
@@ -120,6 +131,12 @@ typedef struct {
   int32_t extra_found_inf; /* overflow flag of the other ranks (the all-reduced flag) */
   int32_t scale_rule;      /* FP8Z1_SCALE_AMAX (0) or FP8Z1_SCALE_POW2 (1) */
   double extra_sumsq;      /* sum of squares of the other ranks' grads (the all-reduced sum) */
+  /* NULL, or a device pointer to the global float64 sum of squares over all
+   * ranks (the all-reduced fp8z1_shard_sumsq outputs), read by the step on
+   * the device when it runs; the step then takes no statistics of its own and
+   * ignores extra_sumsq (extra_found_inf still applies).  Lets the cross-rank
+   * reduction stay on the device, and a captured step see each replay's sum. */
+  const double* d_global_sumsq;
 } fp8z1_hparams;
 
 /* Optimizer step state, 64 bytes, kept in device memory between steps. */
@@ -170,7 +187,9 @@ void fp8z1_table_free(fp8z1_table* table);
  * If slot_sumsq is not NULL (device, 4*shard_slots doubles, 8-byte aligned),
  * the float64 sum of squares of the real elements of each quarter of each
  * slot (rows 32q..32q+31 of slot s at index 4s+q, in a fixed order) is
- * written there as well, in the form fp8z1_step takes as its statistics. */
+ * written there as well, in the form fp8z1_step takes as its statistics.
+ * With dst NULL (FP32 src, slot_sumsq not NULL) only those sums are taken:
+ * the statistics pass over row-major grads that are not folded. */
 int fp8z1_fold(const fp8z1_table* table, const void* const* src, int32_t src_dtype, float* dst, double* slot_sumsq,
                void* stream);
 
@@ -182,12 +201,22 @@ int fp8z1_state_init(const fp8z1_hparams* hp, fp8z1_state* d_state, void* stream
  * squares, one per quarter slot: 32 bytes per slot). */
 int fp8z1_step_workspace_bytes(const fp8z1_table* table, size_t* bytes);
 
+/* This shard's float64 sum of squares of its real grads (level 2 of the
+ * statistics, in the order the step's finalize uses): the sum of d_partials
+ * (device, fp8z1_step_workspace_bytes() bytes written by fp8z1_fold with
+ * slot_sumsq) written to d_sum (device, one double).  Clipping across ranks
+ * ("DeepSpeed ZeRO 优化" section 7) all-reduces these sums; the reduced value
+ * goes to fp8z1_step through hp->d_global_sumsq.  A non-finite grad makes the
+ * sum non-finite, and so the reduced sum, which is the overflow test. */
+int fp8z1_shard_sumsq(const fp8z1_table* table, const double* d_partials, double* d_sum, void* stream);
+
 /* One optimizer step on the shard (section "总结"; step order of
  * "DeepSpeed ZeRO 优化" section 3.2).  All buffers are device memory laid out
  * as the folded shard: grad/master/m/v shard_slots*16384 float32, fp8
  * shard_slots*16384 bytes, scales shard_slots float32.
  *  1. statistics (only if hp->max_grad_norm > 0 or hp->loss_scaling): the
- *     float64 sum of squares of the shard's real grads, plus hp->extra_sumsq;
+ *     float64 sum of squares of the shard's real grads, plus hp->extra_sumsq
+ *     (or the value at hp->d_global_sumsq instead of both);
  *     overflow if that sum is not finite or hp->extra_found_inf is set.
  *     If `presummed` is nonzero, d_workspace already holds the partial sums
  *     from fp8z1_fold(slot_sumsq = d_workspace) of this same grad and the
@@ -205,7 +234,7 @@ int fp8z1_step_workspace_bytes(const fp8z1_table* table, size_t* bytes);
  *     asks for it), code = E4M3(p / scale) (round to nearest even,
  *     saturating at 448, NaN kept); padding codes 0; padding slots scale 1.
  * d_workspace: fp8z1_step_workspace_bytes() bytes (may be NULL when no
- * statistics are taken).  The state at d_state is updated in place. */
+ * statistics are taken or hp->d_global_sumsq is set).  The state at d_state is updated in place. */
 int fp8z1_step(const fp8z1_table* table, const fp8z1_hparams* hp, fp8z1_state* d_state, const float* grad,
                float* master, float* m, float* v, uint8_t* fp8, float* scales, void* d_workspace,
                size_t workspace_bytes, int32_t presummed, void* stream);

@@ -124,6 +124,17 @@ def test_argument_errors_before_any_gpu_work():
         fz.fp8z1_step_rowmajor(t, hp, 16, [18], 16, 16, 16, 16, 16, stream=0)
     with pytest.raises(fz.Fp8z1Error, match="workspace"):
         fz.fp8z1_step_rowmajor(t, hp_clip, 16, [16], 16, 16, 16, 16, 16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="NULL"):
+        fz.fp8z1_fold(t, [16], fz.F32, None, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="statistics-only"):
+        fz.fp8z1_fold(t, [16], fz.BF16, None, slot_sumsq=16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="NULL"):
+        fz.fp8z1_shard_sumsq(t, None, 16, stream=0)
+    with pytest.raises(fz.Fp8z1Error, match="aligned"):
+        fz.fp8z1_shard_sumsq(t, 16, 20, stream=0)
+    hp_glob = fz.Hparams.make(synth.Hparams(max_grad_norm=1.0), global_sumsq=20)
+    with pytest.raises(fz.Fp8z1Error, match="d_global_sumsq"):
+        fz.fp8z1_step(t, hp_glob, 16, 16, 16, 16, 16, 16, 16, stream=0)
     with pytest.raises(fz.Fp8z1Error, match="dtype"):
         fz.fp8z1_unfold(t, 16, fz.BF16, None, [16], stream=0)
     with pytest.raises(fz.Fp8z1Error, match="NULL"):
