@@ -289,8 +289,25 @@ def main() -> int:
             total += BYTES_FOLD_F32 * valid + SLOT_BYTES_FOLD * nslots
         return total, call
 
+    def graph_timed(mode):
+        """The same step captured once into a HIP graph, replayed K times."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            one_step(mode)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        print(f"# {mode} as a graph: {args.steps} replays in {elapsed:.3f}s", file=sys.stderr, flush=True)
+        return elapsed * 1e3 / args.steps
+
     modes = [args.mode, "fold" if args.mode == "fold_on_read" else "fold_on_read"]
     results = {m: timed(m) for m in modes}
+    graph_ms = graph_timed(args.mode)
     st = sh.read_state()
     print(f"# state step {st['step']}", file=sys.stderr, flush=True)
 
@@ -388,6 +405,8 @@ def main() -> int:
         "ceiling": ceiling,
         "alt_mode": {"mode": alt_mode, "ms_per_step": alt_ms, "value": valid / (alt_ms * 1e-3),
                      "per_call_ms": alt_calls, "gbs_algorithmic": alt_total / (alt_ms * 1e-3) / 1e9},
+        "graph": {"mode": args.mode, "ms_per_step": graph_ms, "value": valid / (graph_ms * 1e-3),
+                  "note": "the same step captured into one HIP graph and replayed"},
         "cpu_baseline": cpu,
         "device": _device_info(),
         "source_hash": src_hash,

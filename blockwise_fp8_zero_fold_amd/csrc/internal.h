@@ -28,6 +28,33 @@ struct SlotPlan {
 };
 static_assert(sizeof(SlotPlan) == 32, "SlotPlan is 32 bytes");
 
+// Unfold work item: `rows` consecutive rows of a run of blocks that sit side
+// by side in one block row of a param (consecutive slots, consecutive block
+// columns).  Row i of such a run is one contiguous span of `len` real
+// elements of the param's row-major buffer, so a workgroup can write it with
+// aligned stores whatever the alignment of the row.  `off` is the element
+// offset of the item's first row at the run's first block column, `slot` the
+// run's first slot, `row0` the item's first row within the block row, `soff`
+// the scale offset of the run's first block.
+struct RowItem {
+  int64_t off;
+  int64_t ld;
+  int32_t param;
+  int32_t slot;
+  int32_t len;
+  int32_t nblk;
+  int32_t row0;
+  int32_t rows;
+  int32_t soff;
+  int32_t pad;
+};
+static_assert(sizeof(RowItem) == 48, "RowItem is 48 bytes");
+
+// Size of an unfold work item: all side-by-side blocks of the run (a split
+// run would leave the 128-byte lines at the cut shared by two workgroups),
+// and as many of their rows as fit about kRowItemBytes bytes of FP8 output.
+constexpr int kRowItemBytes = 16384;
+
 enum PtrRole { kRoleFoldSrc = 0, kRoleUnfoldDst = 1, kRoleUnfoldScale = 2, kRoleStepGrad = 3, kNumRoles = 4 };
 
 // Device-side pointer list for one role: a pinned host mirror, the device
@@ -49,6 +76,9 @@ struct fp8z1_table {
   std::mutex mu;
   int device = -1;
   fp8z1::SlotPlan* d_plan = nullptr;
+  fp8z1::RowItem* d_rows = nullptr;  // unfold work items
+  int64_t n_rows = 0;
+  std::vector<char> held;  // per param: the table holds a block of it
   fp8z1::PtrCache ptrs[fp8z1::kNumRoles];
 };
 

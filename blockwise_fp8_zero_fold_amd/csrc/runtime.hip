@@ -2,6 +2,7 @@
 // pointer lists, release; and state copies to and from the host.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 
 #include "internal.h"
@@ -55,6 +56,41 @@ int ensure_device(fp8z1_table* t, void* stream) {
     p.vr = e.vrows;
     p.vc = e.vcols;
   }
+  // unfold work items: runs of side-by-side blocks of one block row, cut into
+  // groups of whole rows of about kRowItemBytes bytes of FP8 output
+  std::vector<RowItem> rows;
+  for (size_t s = 0; s < n;) {
+    const fp8z1_block& e = t->entries[s];
+    if (e.param < 0) {
+      ++s;
+      continue;
+    }
+    size_t s1 = s + 1;
+    while (s1 < n && t->entries[s1].param == e.param && t->entries[s1].expert == e.expert &&
+           t->entries[s1].brow == e.brow && t->entries[s1].bcol == t->entries[s1 - 1].bcol + 1)
+      ++s1;
+    const fp8z1_shape& sh = t->shapes[e.param];
+    const int32_t nblk = static_cast<int32_t>(s1 - s);
+    const int32_t len = kB * (nblk - 1) + t->entries[s1 - 1].vcols;
+    const int32_t vr = e.vrows;
+    const int32_t per = std::max(1, std::min(vr, kRowItemBytes / len));
+    for (int32_t r0 = 0; r0 < vr; r0 += per) {
+      RowItem it;
+      std::memset(&it, 0, sizeof(it));
+      it.off = (int64_t(e.expert) * sh.R + int64_t(kB) * e.brow + r0) * sh.C + int64_t(kB) * e.bcol;
+      it.ld = sh.C;
+      it.param = e.param;
+      it.slot = static_cast<int32_t>(s);
+      it.len = len;
+      it.nblk = nblk;
+      it.row0 = r0;
+      it.rows = std::min(per, vr - r0);
+      it.soff = plan[s].soff;
+      rows.push_back(it);
+    }
+    s = s1;
+  }
+  if (rows.size() > 0x7fffffffULL) return set_error(FP8Z1_ESHAPE, "table: too many unfold work items");
   // (a failed earlier attempt may have left some of these allocated: keep them)
   for (int r = 0; r < kNumRoles; ++r) {
     PtrCache& c = t->ptrs[r];
@@ -75,6 +111,16 @@ int ensure_device(fp8z1_table* t, void* stream) {
     rc = check_hip(hipMemcpy(t->d_plan, plan.data(), n * sizeof(SlotPlan), hipMemcpyHostToDevice), "hipMemcpy(plan)");
     if (rc) return rc;
   }
+  if (!rows.empty()) {
+    if (!t->d_rows)
+      rc = check_hip(hipMalloc(reinterpret_cast<void**>(&t->d_rows), rows.size() * sizeof(RowItem)),
+                     "hipMalloc(unfold items)");
+    if (rc) return rc;
+    rc = check_hip(hipMemcpy(t->d_rows, rows.data(), rows.size() * sizeof(RowItem), hipMemcpyHostToDevice),
+                   "hipMemcpy(unfold items)");
+    if (rc) return rc;
+  }
+  t->n_rows = static_cast<int64_t>(rows.size());
   t->device = dev;
   return FP8Z1_OK;
 }
@@ -111,7 +157,7 @@ using namespace fp8z1;
 
 extern "C" void fp8z1_table_free(fp8z1_table* t) {
   if (!t) return;
-  bool any = t->d_plan != nullptr;
+  bool any = t->d_plan != nullptr || t->d_rows != nullptr;
   for (int r = 0; r < kNumRoles; ++r) any = any || t->ptrs[r].host || t->ptrs[r].dev || t->ptrs[r].done;
   if (any) {  // device resources exist only after a GPU call used the table
     int cur = -1;
@@ -128,6 +174,7 @@ extern "C" void fp8z1_table_free(fp8z1_table* t) {
       if (c.done) (void)hipEventDestroy(static_cast<hipEvent_t>(c.done));
     }
     if (t->d_plan) (void)hipFree(t->d_plan);
+    if (t->d_rows) (void)hipFree(t->d_rows);
     if (t->device >= 0 && cur >= 0 && cur != t->device) (void)hipSetDevice(cur);
   }
   delete t;

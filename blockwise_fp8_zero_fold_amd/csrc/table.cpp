@@ -170,7 +170,11 @@ extern "C" int fp8z1_build_table(const fp8z1_shape* shapes, int32_t n_params, in
   }
 
   int64_t valid = 0;
-  for (const fp8z1_block& e : t->entries) valid += int64_t(e.vrows) * int64_t(e.vcols);
+  t->held.assign(static_cast<size_t>(n_params), 0);
+  for (const fp8z1_block& e : t->entries) {
+    valid += int64_t(e.vrows) * int64_t(e.vcols);
+    if (e.param >= 0) t->held[e.param] = 1;
+  }
   t->info.split = split;
   t->info.dp = dp;
   t->info.rank = rank;

@@ -4,12 +4,15 @@
 // "总结").  Only real positions are written: padding is dropped.
 //
 // As in the fold, whole row segments move (no element transpose).  FP8
-// codes: four workgroups per slot, each a quarter of the block; a 128-byte row
-// segment is 8 lanes of 16-byte stores (streaming when the row is 16-byte
-// aligned, plain unaligned stores otherwise); in a partial block the chunk
-// across the last real column is written byte by byte, so no byte of a
-// neighbouring block's row is ever written.  float32 (used for round-trip
-// checks): one workgroup per slot, the same with 4-element chunks.
+// codes: when every block row segment starts on a 128-byte line, by blocks;
+// otherwise by destination rows: the blocks of one block row that sit side
+// by side in the shard fill one contiguous span of each param row, which a
+// workgroup writes with aligned 16-byte stores at any alignment of the rows
+// (a row segment of one block is 128 bytes, so blockwise stores into such
+// rows would leave most 128-byte lines shared by two workgroups, each
+// writing part of the line).
+// float32 (used for round-trip checks): one workgroup per slot, 4-element
+// chunks at any alignment.
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"
@@ -19,16 +22,84 @@ namespace {
 
 constexpr int kUnfThreads = 256;
 
-// FP8 codes: a workgroup moves a quarter of a block (32 rows x 128 bytes,
-// 4 KB), so that the workgroups in flight cover a compact range of memory.
+// Bytes [sh, sh + 16) of the 32 bytes lo || hi (lo first), sh in [0, 16).
+__device__ __forceinline__ uint4 funnel16(const uint4 lo, const uint4 hi, int sh) {
+  const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  const int q = sh >> 2, r = 8 * (sh & 3);
+  uint32_t e[5];
+#pragma unroll
+  for (int n = 0; n < 5; ++n) e[n] = q == 0 ? d[n] : q == 1 ? d[n + 1] : q == 2 ? d[n + 2] : d[n + 3];
+  // e[n] >> r | e[n + 1] << (32 - r), with r = 0 giving e[n]
+  uint32_t o[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+    o[n] = static_cast<uint32_t>(((static_cast<uint64_t>(e[n + 1]) << 32) | e[n]) >> r);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// FP8 codes, by rows: one workgroup per work item (whole rows of a run of
+// side-by-side blocks, see RowItem).  Row r of the run is `len` contiguous
+// bytes of the param; the workgroup writes it as the 16-byte-aligned chunks
+// that cover it.  Lane chunk k of a row starting m bytes past a 16-byte
+// boundary takes run bytes [16k - m, 16k - m + 16): the folded row segments
+// of the run's blocks are 128-byte runs, so those bytes are the tail of run
+// chunk k - 1 and the head of run chunk k, joined with a funnel shift.
+// Chunks wholly inside the row are one aligned (streaming) store; the first
+// and last chunk of a row are written byte by byte, only the row's own bytes,
+// so no byte outside the run is ever written.
+__global__ __launch_bounds__(kUnfThreads) void unfold_rows_e4m3_kernel(const RowItem* __restrict__ items,
+                                                                       const uint8_t* __restrict__ folded,
+                                                                       void* const* __restrict__ dsts,
+                                                                       const float* __restrict__ scales,
+                                                                       float* const* __restrict__ dscales) {
+  const RowItem it = items[blockIdx.x];
+  const int t = threadIdx.x;
+  if (dscales && it.row0 == 0)
+    for (int b = t; b < it.nblk; b += kUnfThreads) dscales[it.param][it.soff + b] = scales[it.slot + b];
+  uint8_t* base = static_cast<uint8_t*>(dsts[it.param]) + it.off;
+  const uint8_t* src = folded + static_cast<int64_t>(it.slot) * kBlockElems + static_cast<int64_t>(it.row0) * kB;
+  const int len = it.len;
+  const int nq = 8 * it.nblk;        // 16-byte chunks of the run's folded row segments
+  const int kc = (len + 30) / 16;    // chunks a row of len bytes can touch at any alignment
+  const int total = it.rows * kc;
+  for (int c = t; c < total; c += kUnfThreads) {
+    const int r = c / kc, k = c - r * kc;
+    uint8_t* row = base + static_cast<int64_t>(r) * it.ld;
+    const int m = static_cast<int>(reinterpret_cast<uintptr_t>(row) & 15u);
+    const int x0 = 16 * k - m;  // run byte of the chunk's first byte (> -16)
+    if (x0 >= len) continue;
+    const uint8_t* srow = src + r * kB;
+    // run chunk q of row r: block q / 8 of the run, bytes 16 (q % 8) of its row segment
+    auto chunk = [&](int q) -> uint4 {
+      if (q < 0 || q >= nq) return make_uint4(0u, 0u, 0u, 0u);
+      return ld_stream(reinterpret_cast<const uint4*>(srow + static_cast<int64_t>(q >> 3) * kBlockElems +
+                                                      16 * (q & 7)));
+    };
+    const uint4 hi = chunk(k);
+    const uint4 x = m ? funnel16(chunk(k - 1), hi, 16 - m) : hi;
+    uint8_t* d = row + x0;  // 16-byte aligned
+    if (x0 >= 0 && x0 + 16 <= len) {
+      st_stream(reinterpret_cast<uint4*>(d), x);
+    } else {
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+      const int b0 = x0 < 0 ? -x0 : 0, b1 = len - x0 < 16 ? len - x0 : 16;
+      for (int b = b0; b < b1; ++b) d[b] = static_cast<uint8_t>(w[b >> 2] >> (8 * (b & 3)));
+    }
+  }
+}
+
+// FP8 codes, by blocks (used when every row segment of the call starts on a
+// 128-byte line, so no line is shared by two workgroups): a workgroup moves
+// a quarter of a block (32 rows x 128 bytes, 4 KB), so that the workgroups in
+// flight cover a compact range of memory; 8 lanes per row, 16 bytes each.
 constexpr int kUnfRows = 32;
 constexpr int kUnfParts = kB / kUnfRows;
 
-__global__ __launch_bounds__(kUnfThreads) void unfold_e4m3_kernel(const SlotPlan* __restrict__ plan,
-                                                                  const uint8_t* __restrict__ folded,
-                                                                  void* const* __restrict__ dsts,
-                                                                  const float* __restrict__ scales,
-                                                                  float* const* __restrict__ dscales) {
+__global__ __launch_bounds__(kUnfThreads) void unfold_blocks_e4m3_kernel(const SlotPlan* __restrict__ plan,
+                                                                         const uint8_t* __restrict__ folded,
+                                                                         void* const* __restrict__ dsts,
+                                                                         const float* __restrict__ scales,
+                                                                         float* const* __restrict__ dscales) {
   const int64_t s = blockIdx.x / kUnfParts;
   const int part = blockIdx.x % kUnfParts;
   const SlotPlan P = plan[s];
@@ -124,11 +195,22 @@ extern "C" int fp8z1_unfold(const fp8z1_table* ct, const void* folded, int32_t d
   const int64_t n = t->info.shard_slots;
   if (n == 0) return FP8Z1_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == FP8Z1_E4M3)
-    hipLaunchKernelGGL(unfold_e4m3_kernel, dim3(n * kUnfParts), dim3(kUnfThreads), 0, s, t->d_plan,
-                       static_cast<const uint8_t*>(folded), ddst, with_scales ? scales : nullptr,
-                       reinterpret_cast<float* const*>(dsc));
-  else
+  if (dtype == FP8Z1_E4M3) {
+    // by blocks when every held param's rows and block row segments start on
+    // a 128-byte line (C a multiple of 128, destination 128-byte aligned),
+    // else by rows
+    bool lines = true;
+    for (size_t p = 0; p < t->shapes.size() && lines; ++p)
+      if (t->held[p]) lines = t->shapes[p].C % 128 == 0 && reinterpret_cast<uintptr_t>(dst[p]) % 128 == 0;
+    if (lines)
+      hipLaunchKernelGGL(unfold_blocks_e4m3_kernel, dim3(n * kUnfParts), dim3(kUnfThreads), 0, s, t->d_plan,
+                         static_cast<const uint8_t*>(folded), ddst, with_scales ? scales : nullptr,
+                         reinterpret_cast<float* const*>(dsc));
+    else if (t->n_rows > 0)
+      hipLaunchKernelGGL(unfold_rows_e4m3_kernel, dim3(static_cast<unsigned>(t->n_rows)), dim3(kUnfThreads), 0, s,
+                         t->d_rows, static_cast<const uint8_t*>(folded), ddst, with_scales ? scales : nullptr,
+                         reinterpret_cast<float* const*>(dsc));
+  } else
     hipLaunchKernelGGL(unfold_f32_kernel, dim3(n), dim3(kUnfThreads), 0, s, t->d_plan,
                        static_cast<const float*>(folded), ddst, with_scales ? scales : nullptr,
                        reinterpret_cast<float* const*>(dsc));

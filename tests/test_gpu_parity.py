@@ -117,6 +117,60 @@ def test_fold_unfold_bit_exact(name, split):
         t.free()
 
 
+@pytest.mark.parametrize("name", ["moe_small", "ragged_small", "full_small"])
+def test_unfold_codes_at_any_destination_alignment(name):
+    """FP8 unfold of random codes (padding bytes random too: they must be dropped) into
+    destinations at byte offsets 0, 1, 16, 64 and 127 of a sentinel-filled buffer: the
+    shard's real positions get the oracle's bytes, no other byte (inside the param or in
+    the margins around it) changes; scales land in [E, Rb, Cb].  Covers both unfold
+    kernels (by blocks when rows start on 128-byte lines, by rows otherwise)."""
+    gh = _gh()
+    w = synth.get(name)
+    rng = np.random.default_rng(17)
+    for r in (0, w.dp - 1, otable.ALL_RANKS):
+        tab = otable.build(w.shapes, w.dp, r)
+        t = fz.fp8z1_build_table(w.shapes, w.dp, r)
+        n = t.shard_slots
+        held = gh.held_experts(tab["entries"])
+        folded = rng.integers(0, 256, size=(n, 128, 128), dtype=np.uint8)
+        fsc = rng.random(n).astype(np.float32)
+        d_folded = torch.from_numpy(folded.reshape(-1)).cuda()
+        d_fsc = torch.from_numpy(fsc).cuda()
+        want = {p: np.zeros(s, np.uint8) for p, s in enumerate(w.shapes)}
+        want_s = {p: np.zeros(otable.grid(s), np.float32) for p, s in enumerate(w.shapes)}
+        layout.unfold_shard(tab, folded, want, fsc, want_s)
+        mask = {p: np.zeros(s, bool) for p, s in enumerate(w.shapes)}
+        layout.unfold_shard(tab, layout.valid_mask(tab), mask)
+        for off in (0, 1, 16, 64, 127):
+            bufs, outs, souts = {}, [], []
+            for p, s in enumerate(w.shapes):
+                if p not in held:
+                    outs.append(None)
+                    souts.append(None)
+                    continue
+                size = int(np.prod(s))
+                bufs[p] = torch.full((size + 256,), 0xA5, dtype=torch.uint8, device="cuda")
+                outs.append(bufs[p][off:off + size])
+                souts.append(torch.full(otable.grid(s), float("nan"), dtype=torch.float32, device="cuda"))
+            fz.fp8z1_unfold(t, d_folded, fz.E4M3, d_fsc, outs, souts)
+            torch.cuda.synchronize()
+            for p in held:
+                b = bufs[p].cpu().numpy()
+                size = int(np.prod(w.shapes[p]))
+                assert (b[:off] == 0xA5).all() and (b[off + size:] == 0xA5).all(), (r, off, p, "margin")
+                got = b[off:off + size].reshape(w.shapes[p])
+                assert (got[mask[p]] == want[p][mask[p]]).all(), (r, off, p)
+                assert (got[~mask[p]] == 0xA5).all(), (r, off, p, "outside the shard")
+                blocks = np.zeros(otable.grid(w.shapes[p]), bool)
+                for e in tab["entries"]:
+                    if e["param"] == p:
+                        blocks[int(e["expert"]), int(e["brow"]), int(e["bcol"])] = True
+                gs = souts[p].cpu().numpy()
+                assert gh.bits_equal(gs[blocks], want_s[p][blocks]), (r, off, p, "scales")
+                assert np.isnan(gs[~blocks]).all(), (r, off, p, "scales outside the shard")
+        t.free()
+
+
 @pytest.mark.parametrize("name", ["tiny", "ragged_small", "moe_small"])
 def test_fused_statistics_equal_separate_kernel(name):
     """Per-slot sums of squares written by the fold equal the separate statistics
