@@ -24,6 +24,8 @@ constexpr int kChunksPerRow = kB / 4;
 // t + 768 in increasing order, the 4 elements of a chunk in increasing order,
 // then the block reduction below combines the 256 thread sums in a fixed order.
 constexpr int kSumThreads = 256;
+// XCDs of the part; consecutive workgroups of a launch are dealt to them in turn
+constexpr int kXcds = 8;
 constexpr int kStatParts = FP8Z1_STAT_PARTS;
 static_assert(kB % kStatParts == 0 && (kChunks / kStatParts) % kSumThreads == 0, "part split");
 constexpr int kPartRows = kB / kStatParts;

@@ -20,6 +20,11 @@ namespace {
 
 constexpr int kFoldThreads = kSumThreads;  // also the statistics order
 
+// workgroups of a fold launch: one per quarter slot, rounded up to whole XCD rounds
+inline unsigned fold_grid(int64_t nslots) {
+  return static_cast<unsigned>((nslots * kStatParts + kXcds - 1) / kXcds * kXcds);
+}
+
 template <typename T>
 struct Src;
 // load4: four consecutive elements from an element-aligned address (one vector
@@ -48,10 +53,17 @@ template <typename T, bool SUMSQ, bool WRITE = true>
 __global__ __launch_bounds__(kFoldThreads) void fold_kernel(const SlotPlan* __restrict__ plan,
                                                             const void* const* __restrict__ srcs,
                                                             float* __restrict__ dst,
-                                                            double* __restrict__ part_sumsq) {
+                                                            double* __restrict__ part_sumsq, int64_t nslots) {
   __shared__ double red[kFoldThreads / 64];
-  const int64_t s = blockIdx.x / kStatParts;
-  const int part = blockIdx.x % kStatParts;
+  // quarter slot of this workgroup: the dispatcher deals workgroups to the 8
+  // XCDs in turn, so XCD x gets a contiguous range of quarter slots and
+  // neighbouring blocks (which may share 128-byte lines of an unaligned
+  // source row) go through one L2
+  const int64_t per_xcd = static_cast<int64_t>(gridDim.x) / kXcds;  // the grid is a multiple of kXcds
+  const int64_t q = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  const int64_t s = q / kStatParts;
+  const int part = static_cast<int>(q % kStatParts);
+  if (s >= nslots) return;  // whole workgroup
   const SlotPlan P = plan[s];
   float4* out = WRITE ? reinterpret_cast<float4*>(dst + s * kBlockElems) + part * kPartChunks : nullptr;
   const int t = threadIdx.x;
@@ -115,11 +127,12 @@ template <typename T>
 hipError_t launch(const SlotPlan* plan, void** srcs, float* dst, double* sumsq, int64_t nslots,
                   hipStream_t stream) {
   if (nslots == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(nslots * kStatParts));
+  const dim3 grid(fold_grid(nslots));
   if (sumsq)
-    hipLaunchKernelGGL((fold_kernel<T, true>), grid, dim3(kFoldThreads), 0, stream, plan, srcs, dst, sumsq);
+    hipLaunchKernelGGL((fold_kernel<T, true>), grid, dim3(kFoldThreads), 0, stream, plan, srcs, dst, sumsq, nslots);
   else
-    hipLaunchKernelGGL((fold_kernel<T, false>), grid, dim3(kFoldThreads), 0, stream, plan, srcs, dst, sumsq);
+    hipLaunchKernelGGL((fold_kernel<T, false>), grid, dim3(kFoldThreads), 0, stream, plan, srcs, dst, sumsq,
+                       nslots);
   return hipGetLastError();
 }
 
@@ -127,8 +140,8 @@ hipError_t launch(const SlotPlan* plan, void** srcs, float* dst, double* sumsq, 
 
 hipError_t launch_grad_sumsq(const SlotPlan* plan, void** grads, double* sumsq, int64_t nslots, hipStream_t stream) {
   if (nslots == 0) return hipSuccess;
-  hipLaunchKernelGGL((fold_kernel<float, true, false>), dim3(static_cast<unsigned>(nslots * kStatParts)),
-                     dim3(kFoldThreads), 0, stream, plan, grads, nullptr, sumsq);
+  hipLaunchKernelGGL((fold_kernel<float, true, false>), dim3(fold_grid(nslots)), dim3(kFoldThreads), 0, stream, plan,
+                     grads, nullptr, sumsq, nslots);
   return hipGetLastError();
 }
 

@@ -184,6 +184,8 @@ __global__ void state_init_kernel(fp8z1_state* st, float loss_scale) {
 struct UpdateArgs {
   float beta1, beta2, one_minus_beta1, one_minus_beta2, eps;
   int32_t pow2_scale;
+  int64_t nslots;
+  int32_t xcd_ranges;  // 1: XCD x takes a contiguous range of slots (grid = whole XCD rounds)
 };
 
 // Block scale from the block's amax.  Default: amax / 448 (the largest E4M3
@@ -270,7 +272,11 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
   if (st->found_inf) return;  // skipped step: nothing changes
   const float k = st->k, decay = st->decay, step_size = st->step_size, bc2 = st->bc2_sqrt;
 
-  const int64_t s = blockIdx.x;
+  int64_t s = blockIdx.x;
+  if (a.xcd_ranges) {
+    s = (blockIdx.x % kXcds) * (static_cast<int64_t>(gridDim.x) / kXcds) + blockIdx.x / kXcds;
+    if (s >= a.nslots) return;  // whole workgroup
+  }
   const SlotPlan P = plan[s];
   const int t = threadIdx.x;
   uint32_t* codes = reinterpret_cast<uint32_t*>(fp8 + s * kBlockElems);
@@ -498,11 +504,22 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
   ua.one_minus_beta2 = static_cast<float>(1.0 - static_cast<double>(hp->beta2));
   ua.eps = hp->eps;
   ua.pow2_scale = hp->scale_rule == FP8Z1_SCALE_POW2 ? 1 : 0;
+  ua.nslots = n;
+  // Row-major grads whose block row segments do not start on 128-byte lines
+  // share a line between neighbouring blocks; giving each XCD a contiguous
+  // slot range fetches such a line into one L2 instead of two.  Otherwise the
+  // plain order keeps the workgroups in flight on one compact window.
+  ua.xcd_ranges = 0;
   if (grad_rows)
-    hipLaunchKernelGGL(update_kernel<true>, dim3(n), dim3(kUpdThreads), 0, s, t->d_plan, d_state, nullptr, drows,
+    for (size_t p = 0; p < t->shapes.size() && !ua.xcd_ranges; ++p)
+      if (t->held[p])
+        ua.xcd_ranges = t->shapes[p].C % 32 != 0 || reinterpret_cast<uintptr_t>(grad_rows[p]) % 128 != 0;
+  const unsigned grid = static_cast<unsigned>(ua.xcd_ranges ? (n + kXcds - 1) / kXcds * kXcds : n);
+  if (grad_rows)
+    hipLaunchKernelGGL(update_kernel<true>, dim3(grid), dim3(kUpdThreads), 0, s, t->d_plan, d_state, nullptr, drows,
                        master, m, v, fp8, scales, ua);
   else
-    hipLaunchKernelGGL(update_kernel<false>, dim3(n), dim3(kUpdThreads), 0, s, t->d_plan, d_state, grad, nullptr,
+    hipLaunchKernelGGL(update_kernel<false>, dim3(grid), dim3(kUpdThreads), 0, s, t->d_plan, d_state, grad, nullptr,
                        master, m, v, fp8, scales, ua);
   return check_hip(hipGetLastError(), "step: update launch");
 }
