@@ -507,6 +507,25 @@ def test_extreme_shapes_and_all_padding_ranks():
     _run_parity(few, fold_on_read=True)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_shape_sets(seed):
+    """Random sets of 1-5 params (E 1-3, R and C 1-400, so most rows start off any
+    alignment), random DP, split, clipping / loss scaling and scale rule: the whole step
+    on both routes, every rank listed, bit for bit against the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    k = int(rng.integers(1, 6))
+    shapes = tuple((int(rng.integers(1, 4)), int(rng.integers(1, 401)), int(rng.integers(1, 401))) for _ in range(k))
+    dp = int(rng.integers(1, 7))
+    hp = synth.Hparams(max_grad_norm=float(rng.choice([0.0, 0.05, 1.0])), loss_scaling=bool(rng.integers(0, 2)),
+                       init_scale=256.0, growth_interval=1, scale_rule=int(rng.integers(0, 2)))
+    w = synth.Workload(name=f"random{seed}", shapes=shapes, dp=dp, ranks=tuple(range(dp)), steps=2, hp=hp,
+                       split=str(rng.choice(["block", "param"])), grad_sigma=1e-3,
+                       grad_premult=256.0 if hp.loss_scaling else 1.0)
+    print(f"# {w.name}: shapes {shapes} dp {dp} split {w.split} hp {hp}", flush=True)
+    _run_parity(w)
+    _run_parity(w, fold_on_read=True)
+
+
 def test_c_abi_consumer_without_python(tmp_path):
     """A C++ program (tests/native/abi_c_step.cpp, built with the library) drives the
     ABI with its own HIP allocations and stream, no torch in the process; its outputs
