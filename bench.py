@@ -116,14 +116,15 @@ def _traffic(workload: str, mode: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, rank: int, slots: int, steps: int = 2):
+def cpu_baseline(w, rank: int, slots: int, steps: int = 2, first: int = 0):
     """The oracle (numpy, as committed) on a bounded sample of the same shard: per step
-    fold of the grads, the step, unfold of the codes, over the first ``slots`` slots."""
+    fold of the grads, the step, unfold of the codes, over ``slots`` slots from ``first``."""
     from oracle import layout, optim, step, table
 
     tab = table.build(w.shapes, w.dp, rank, table.PARAM if w.split == "param" else table.BLOCK)
     sub = dict(tab)
-    sub["entries"] = tab["entries"][:slots]
+    sub["entries"] = tab["entries"][first:first + slots]
+    slots = len(sub["entries"])
     sub["shard_slots"] = slots
     held = _held(sub["entries"])
     G = {p: np.zeros(w.shapes[p], np.float32) for p in held}
@@ -149,6 +150,66 @@ def cpu_baseline(w, rank: int, slots: int, steps: int = 2):
     return valid / dt, valid, dt
 
 
+def _cpu_worker(job):
+    """One worker of the parallel oracle run (a fresh process, no GPU use)."""
+    name, split, rank, first, slots, steps, barrier = job
+    w = synth.get(name).with_(split=split)
+    barrier.wait()
+    t0 = time.perf_counter()
+    rate, valid, dt = cpu_baseline(w, rank, slots, steps=steps, first=first)
+    return valid, dt, time.perf_counter() - t0
+
+
+def cpu_baseline_parallel(w, rank: int, nslots: int, procs: int, steps: int = 2):
+    """The same oracle in ``procs`` worker processes, each on its own contiguous slot
+    range, together covering the whole shard; elements/s = real elements of the shard
+    / the slowest worker's time per step.  Workers start from a clean interpreter
+    (spawn) and never touch the GPU; each keeps its own clipping statistics (the
+    timed work is the same)."""
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    per = -(-nslots // procs)
+    ranges = [(i * per, min(per, nslots - i * per)) for i in range(procs) if i * per < nslots]
+    mgr = ctx.Manager()
+    barrier = mgr.Barrier(len(ranges))
+    with ctx.Pool(len(ranges)) as pool:
+        res = pool.map(_cpu_worker, [(w.name, w.split, rank, a, n, steps, barrier) for a, n in ranges])
+    mgr.shutdown()
+    valid = sum(r[0] for r in res)
+    dt = max(r[1] for r in res)
+    return valid / dt, valid, dt, len(ranges)
+
+
+def _host_info() -> dict:
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "cpus_visible": os.cpu_count()}
+
+
+def _table_info(w, rank: int) -> dict:
+    """Host table build time and padding of both splits (the reason for the param split
+    is less padding per rank; its cost is every rank padded to the largest bucket)."""
+    import blockwise_fp8_zero_fold_amd as fz
+    out = {}
+    for name, split in (("block", fz.SPLIT_BLOCK), ("param", fz.SPLIT_PARAM)):
+        t0 = time.perf_counter()
+        t = fz.fp8z1_build_table(w.shapes, w.dp, rank, split)
+        ms = (time.perf_counter() - t0) * 1e3
+        a = fz.fp8z1_build_table(w.shapes, w.dp, fz.ALL_RANKS, split)
+        out[name] = {"build_ms": ms, "rank_slots": t.shard_slots,
+                     "rank_pad_frac": t.info["pad_elems"] / max(1, t.shard_slots * BLOCK),
+                     "all_ranks_pad_frac": a.info["pad_elems"] / max(1, a.shard_slots * BLOCK)}
+        t.free()
+        a.free()
+    return out
+
+
 def _device_info() -> dict:
     """What identifies the GPU and its memory set-up (bandwidth differs between parts)."""
     import glob
@@ -160,6 +221,15 @@ def _device_info() -> dict:
     uuid = getattr(pr, "uuid", None)
     if uuid is not None:
         info["uuid"] = str(uuid)
+    for key in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):  # the current level is marked '*'
+        for f in sorted(glob.glob(f"/sys/class/drm/card*/device/{key}")):
+            try:
+                cur = [ln.split(":", 1)[1].strip(" *\n") for ln in open(f) if ln.rstrip().endswith("*")]
+                if cur:
+                    info[key.replace("pp_dpm_", "clock_")] = cur[0]
+                    break
+            except (OSError, IndexError):
+                pass
     for key in ("current_memory_partition", "current_compute_partition"):
         for f in sorted(glob.glob(f"/sys/class/drm/card*/device/{key}")):
             try:
@@ -168,6 +238,57 @@ def _device_info() -> dict:
             except OSError:
                 pass
     return info
+
+
+def sweep_ranks(w, args) -> int:
+    """The fold-on-read step (update + requant, then unfold) on every rank's shard in
+    turn, each with its own inputs; one JSON line with per-rank times."""
+    import torch
+
+    import blockwise_fp8_zero_fold_amd as fz
+    from blockwise_fp8_zero_fold_amd.shard import Shard
+    split = fz.SPLIT_PARAM if w.split == "param" else fz.SPLIT_BLOCK
+    hp = fz.Hparams.make(w.hp)
+    stream = torch.cuda.current_stream()
+    rows = []
+    for r in range(w.dp):
+        sh = Shard(w.shapes, w.dp, r, split)
+        held = _held(sh.table.entries())
+        weights = _gen_params(w, held, lambda p, e: synth.master_slab(w, p, e), torch.float32)
+        sh.init(hp, weights, fz.F32)
+        del weights
+        grads = _gen_params(w, held, lambda p, e: synth.grad_slab(w, p, e, 1), torch.float32)
+        codes = [torch.zeros(s, dtype=torch.uint8, device="cuda") if p in held else None
+                 for p, s in enumerate(w.shapes)]
+        scales = [torch.zeros((s[0], -(-s[1] // 128), -(-s[2] // 128)), dtype=torch.float32, device="cuda")
+                  if p in held else None for p, s in enumerate(w.shapes)]
+        for _ in range(args.warmup):
+            sh.step(hp, grads, codes, scales, fold_on_read=True)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for e in ev:
+            e[0].record(stream)
+            sh.update_rowmajor(hp, grads)
+            e[1].record(stream)
+            sh.unfold(codes, scales)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        valid = sh.table.info["valid_elems"]
+        rows.append({"rank": r, "slots": sh.n_slots, "valid_elems": valid, "ms_per_step": ms,
+                     "step_ms": float(np.mean([e[0].elapsed_time(e[1]) for e in ev])),
+                     "unfold_ms": float(np.mean([e[1].elapsed_time(e[2]) for e in ev])),
+                     "elems_per_s": valid / (ms * 1e-3)})
+        print(f"# rank {r}: {ms:.4f} ms per step", file=sys.stderr, flush=True)
+        del sh, grads, codes, scales
+        torch.cuda.empty_cache()
+    ms_all = sorted(x["ms_per_step"] for x in rows)
+    print(json.dumps({"sweep": "ranks", "workload": w.name, "dp": w.dp, "steps": args.steps, "warmup": args.warmup,
+                      "route": "fold on read", "per_rank": rows, "min_ms": ms_all[0],
+                      "median_ms": float(np.median(ms_all)), "max_ms": ms_all[-1], "device": _device_info(),
+                      "source_hash": _source_hash()}), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -184,6 +305,9 @@ def main() -> int:
     ap.add_argument("--unfused-stats", action="store_true", help="separate statistics kernel instead of fold-fused")
     ap.add_argument("--cpu-slots", type=int, default=16384, help="oracle sample size (slots) for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-ranks", action="store_true",
+                    help="time the fold-on-read step on every rank's shard of the workload in turn and print one "
+                         "JSON line with per-rank times (min / median / max); not the headline line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run torch's plain copy of 2 x 1 GiB five times (the reference kernel whose "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic of the step kernels)")
@@ -192,6 +316,31 @@ def main() -> int:
         print(f"bench.py: one GPU only (asked for --gpus {args.gpus}): the path runs one data-parallel rank's "
               "shard; collectives across GPUs are not part of it", file=sys.stderr)
         return 2
+
+    w = synth.get(args.workload)
+    if args.split:
+        w = w.with_(split=args.split)
+    rank = w.ranks[0]
+
+    # The oracle baselines run first, before this process touches the GPU (the
+    # parallel one starts worker processes).
+    cpu = cpu_par = None
+    if not (args.no_cpu_baseline or args.calibrate_copy or args.sweep_ranks):
+        from oracle import table as otable
+        n_all = otable.build(w.shapes, w.dp, rank, otable.PARAM if w.split == "param" else otable.BLOCK)["shard_slots"]
+        slots = min(args.cpu_slots, n_all)
+        print(f"# cpu baseline: oracle on {slots} slots, one process", file=sys.stderr, flush=True)
+        rate, n_el, dt = cpu_baseline(w, rank, slots, steps=2)
+        cpu = {"value": rate, "unit": "elements/s", "cores": 1, "kind": "oracle",
+               "sample": f"2 steps of fold+step+unfold over the first {slots} slots ({n_el} real elements) of the "
+                         f"same shard, numpy, one thread, {dt:.1f}s per step", "host": _host_info()}
+        procs = _threads()
+        print(f"# cpu baseline: oracle on all {n_all} slots, {procs} processes", file=sys.stderr, flush=True)
+        rate, n_el, dt, used = cpu_baseline_parallel(w, rank, n_all, procs, steps=2)
+        cpu_par = {"value": rate, "unit": "elements/s", "cores": used, "kind": "oracle",
+                   "sample": f"2 steps of fold+step+unfold over the whole shard ({n_el} real elements), split into "
+                             f"{used} contiguous slot ranges, one numpy process each, {dt:.2f}s per step (slowest "
+                             "process)", "host": _host_info()}
 
     import torch
 
@@ -209,10 +358,8 @@ def main() -> int:
     import blockwise_fp8_zero_fold_amd as fz
     from blockwise_fp8_zero_fold_amd.shard import Shard
 
-    w = synth.get(args.workload)
-    if args.split:
-        w = w.with_(split=args.split)
-    rank = w.ranks[0]
+    if args.sweep_ranks:
+        return sweep_ranks(w, args)
     split = fz.SPLIT_PARAM if w.split == "param" else fz.SPLIT_BLOCK
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()
@@ -308,6 +455,17 @@ def main() -> int:
     modes = [args.mode, "fold" if args.mode == "fold_on_read" else "fold_on_read"]
     results = {m: timed(m) for m in modes}
     graph_ms = graph_timed(args.mode)
+
+    skip = None
+    if stats:
+        # a skipped step (overflow reported by the other ranks): statistics and
+        # finalize run, the update exits at once, the unfold rewrites the codes
+        hp_run = hp
+        hp = fz.Hparams.make(w.hp, extra_found_inf=True)
+        _, skip_calls = timed(args.mode)
+        hp = hp_run
+        skip = {"mode": args.mode, "per_call_ms": skip_calls,
+                "note": "skipped steps (overflow flag from the other ranks): statistics + finalize, no update"}
     st = sh.read_state()
     print(f"# state step {st['step']}", file=sys.stderr, flush=True)
 
@@ -354,15 +512,6 @@ def main() -> int:
     print(f"# ceilings: update pattern {ceiling['update_pattern_gbs']:.0f} GB/s, copy {ceiling['copy_gbs']:.0f} GB/s, "
           f"copy by spread {({k: round(v) for k, v in spread_gbs.items()})}", file=sys.stderr, flush=True)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        slots = min(args.cpu_slots, nslots)
-        print(f"# cpu baseline: oracle on {slots} slots", file=sys.stderr, flush=True)
-        rate, n_el, dt = cpu_baseline(w, rank, slots, steps=2)
-        cpu = {"value": rate, "unit": "elements/s", "cores": 1, "kind": "oracle",
-               "sample": f"2 steps of fold+step+unfold over the first {slots} slots ({n_el} real elements) of the "
-                         f"same shard, numpy, one thread, {dt:.1f}s per step"}
-
     out = {
         "metric": "optimizer-step elements/s and GB/s (% of HBM peak) per 1-GPU shard",
         "value": valid / (ms_per_step * 1e-3),
@@ -405,9 +554,12 @@ def main() -> int:
         "ceiling": ceiling,
         "alt_mode": {"mode": alt_mode, "ms_per_step": alt_ms, "value": valid / (alt_ms * 1e-3),
                      "per_call_ms": alt_calls, "gbs_algorithmic": alt_total / (alt_ms * 1e-3) / 1e9},
+        "skip_step": skip,
         "graph": {"mode": args.mode, "ms_per_step": graph_ms, "value": valid / (graph_ms * 1e-3),
                   "note": "the same step captured into one HIP graph and replayed"},
         "cpu_baseline": cpu,
+        "cpu_baseline_parallel": cpu_par,
+        "table": _table_info(w, rank),
         "device": _device_info(),
         "source_hash": src_hash,
     }
