@@ -1,18 +1,24 @@
 // A C-ABI consumer with no Python and no torch: it drives libfp8z1 through
 // include/fp8z1.h with its own HIP allocations and stream.
 //
-//   abi_c_step <dir>
+//   abi_c_step <dir> [graph]
 //
 // <dir>/meta.txt:  n_params dp rank steps
 //                  E R C                      (n_params lines)
 //                  lr beta1 beta2 eps wd max_grad_norm
+//                  loss_scaling init_scale growth_factor backoff_factor growth_interval scale_rule
 //                  extra_sumsq                (one line per step)
 // <dir>/master_<p>.bin  float32 [E,R,C] for every param
 // <dir>/grad_<t>_<p>.bin float32 [E,R,C] for every step t (1-based) and param
 // Writes <dir>/out_master.bin (the folded FP32 master shard), out_codes_<p>.bin
 // and out_scales_<p>.bin (row-major codes and [E,Rb,Cb] scales after the last
 // step; positions the shard does not hold stay 0), out_state.txt.
-// The step reads the row-major grads (fp8z1_step_rowmajor).
+// The step reads the row-major grads (fp8z1_step_rowmajor).  With "graph"
+// (a single rank, extra_sumsq 0): step 1 runs as plain calls -- the
+// statistics-only pass, fp8z1_shard_sumsq into a device double, the step
+// reading that sum through hp.d_global_sumsq, the unfold -- then the same
+// calls are captured once into a HIP graph, and every later step copies its
+// grads into the captured buffers and launches the graph.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -58,8 +64,9 @@ static void write_file(const std::string& path, const void* data, size_t bytes) 
 }
 
 int main(int argc, char** argv) {
-  if (argc != 2) return 1;
+  if (argc != 2 && argc != 3) return 1;
   const std::string dir = argv[1];
+  const bool graph = argc == 3 && std::string(argv[2]) == "graph";
   FILE* m = std::fopen((dir + "/meta.txt").c_str(), "r");
   if (!m) return 2;
   int n, dp, rank, steps;
@@ -71,14 +78,13 @@ int main(int argc, char** argv) {
   if (std::fscanf(m, "%f %f %f %f %f %f", &hp.lr, &hp.beta1, &hp.beta2, &hp.eps, &hp.weight_decay,
                   &hp.max_grad_norm) != 6)
     return 2;
+  if (std::fscanf(m, "%d %f %f %f %d %d", &hp.loss_scaling, &hp.init_scale, &hp.growth_factor, &hp.backoff_factor,
+                  &hp.growth_interval, &hp.scale_rule) != 6)
+    return 2;
   std::vector<double> extra(steps);
   for (auto& x : extra)
     if (std::fscanf(m, "%lf", &x) != 1) return 2;
   std::fclose(m);
-  hp.growth_factor = 2.0f;
-  hp.backoff_factor = 0.5f;
-  hp.growth_interval = 1000;
-  hp.init_scale = 1.0f;
 
   fp8z1_table* table = nullptr;
   CHECK(fp8z1_build_table(shapes.data(), n, dp, rank, FP8Z1_SPLIT_BLOCK, &table));
@@ -92,13 +98,17 @@ int main(int argc, char** argv) {
   uint8_t* fp8;
   float* scales;
   double* ws;
+  double* glob;
   fp8z1_state* state;
+  size_t wsb = 0;
+  CHECK(fp8z1_step_workspace_bytes(table, &wsb));
   CHECK_HIP(hipMalloc(&master, el * 4));
   CHECK_HIP(hipMalloc(&mom1, el * 4));
   CHECK_HIP(hipMalloc(&mom2, el * 4));
   CHECK_HIP(hipMalloc(&fp8, el));
   CHECK_HIP(hipMalloc(&scales, slots * 4 + 4));
-  CHECK_HIP(hipMalloc(&ws, slots * 8 + 8));
+  CHECK_HIP(hipMalloc(&ws, wsb + 8));
+  CHECK_HIP(hipMalloc(&glob, sizeof(double)));
   CHECK_HIP(hipMalloc(&state, sizeof(fp8z1_state)));
   CHECK_HIP(hipMemset(mom1, 0, el * 4));
   CHECK_HIP(hipMemset(mom2, 0, el * 4));
@@ -120,20 +130,43 @@ int main(int argc, char** argv) {
 
   CHECK(fp8z1_fold(table, const_cast<const void* const*>(params.data()), FP8Z1_F32, master, nullptr, stream));
   CHECK(fp8z1_state_init(&hp, state, stream));
-  size_t wsb = 0;
-  CHECK(fp8z1_step_workspace_bytes(table, &wsb));
+  const void* const* gl = const_cast<const void* const*>(grads.data());
+  float* const* sl = reinterpret_cast<float* const*>(pscales.data());
+  // one step of the device-statistics sequence (graph mode)
+  fp8z1_hparams hpg = hp;
+  hpg.d_global_sumsq = glob;
+  auto device_stats_step = [&]() {
+    CHECK(fp8z1_fold(table, gl, FP8Z1_F32, nullptr, ws, stream));
+    CHECK(fp8z1_shard_sumsq(table, ws, glob, stream));
+    CHECK(fp8z1_step_rowmajor(table, &hpg, state, gl, master, mom1, mom2, fp8, scales, nullptr, 0, stream));
+    CHECK(fp8z1_unfold(table, fp8, FP8Z1_E4M3, scales, codes.data(), sl, stream));
+  };
+  hipGraphExec_t exec = nullptr;
   for (int t = 1; t <= steps; ++t) {
     for (int p = 0; p < n; ++p) {
       auto h = read_file(dir + "/grad_" + std::to_string(t) + "_" + std::to_string(p) + ".bin", nel[p] * 4);
       CHECK_HIP(hipMemcpyAsync(grads[p], h.data(), nel[p] * 4, hipMemcpyHostToDevice, stream));
       CHECK_HIP(hipStreamSynchronize(stream));
     }
-    hp.extra_sumsq = extra[t - 1];
-    CHECK(fp8z1_step_rowmajor(table, &hp, state, const_cast<const void* const*>(grads.data()), master, mom1, mom2,
-                              fp8, scales, ws, wsb, stream));
-    CHECK(fp8z1_unfold(table, fp8, FP8Z1_E4M3, scales, codes.data(), reinterpret_cast<float* const*>(pscales.data()),
-                       stream));
+    if (!graph) {
+      hp.extra_sumsq = extra[t - 1];
+      CHECK(fp8z1_step_rowmajor(table, &hp, state, gl, master, mom1, mom2, fp8, scales, ws, wsb, stream));
+      CHECK(fp8z1_unfold(table, fp8, FP8Z1_E4M3, scales, codes.data(), sl, stream));
+    } else if (t == 1) {
+      device_stats_step();  // sets the table up and uploads these pointer lists
+      CHECK_HIP(hipStreamSynchronize(stream));
+      hipGraph_t g;
+      CHECK_HIP(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
+      device_stats_step();
+      CHECK_HIP(hipStreamEndCapture(stream, &g));
+      CHECK_HIP(hipGraphInstantiate(&exec, g, nullptr, nullptr, 0));
+      CHECK_HIP(hipGraphDestroy(g));
+    } else {
+      CHECK_HIP(hipGraphLaunch(exec, stream));
+      CHECK_HIP(hipStreamSynchronize(stream));
+    }
   }
+  if (exec) CHECK_HIP(hipGraphExecDestroy(exec));
   fp8z1_state st;
   CHECK(fp8z1_state_read(state, &st, stream));
 
@@ -162,8 +195,9 @@ int main(int argc, char** argv) {
   CHECK_HIP(hipFree(fp8));
   CHECK_HIP(hipFree(scales));
   CHECK_HIP(hipFree(ws));
+  CHECK_HIP(hipFree(glob));
   CHECK_HIP(hipFree(state));
   CHECK_HIP(hipStreamDestroy(stream));
-  std::printf("abi_c_step ok: %zu slots, %d steps\n", slots, steps);
+  std::printf("abi_c_step ok: %zu slots, %d steps%s\n", slots, steps, graph ? ", graph" : "");
   return 0;
 }

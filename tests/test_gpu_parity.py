@@ -526,16 +526,18 @@ def test_random_shape_sets(seed):
     _run_parity(w, fold_on_read=True)
 
 
-def test_c_abi_consumer_without_python(tmp_path):
+@pytest.mark.parametrize("name,rank,mode", [("tiny_clip", 1, "eager"), ("full_small", 0, "graph")])
+def test_c_abi_consumer_without_python(tmp_path, name, rank, mode):
     """A C++ program (tests/native/abi_c_step.cpp, built with the library) drives the
     ABI with its own HIP allocations and stream, no torch in the process; its outputs
-    equal the oracle's."""
+    equal the oracle's.  "graph": the statistics go through fp8z1_shard_sumsq and
+    hp.d_global_sumsq, and steps 2.. are launches of one captured HIP graph (the
+    full_small set: clipping, loss scaling and a skipped step among the replays)."""
     import subprocess
     exe = os.path.join(os.path.dirname(__file__), "native", "abi_c_step")
     if not os.path.exists(exe):
         pytest.fail("tests/native/abi_c_step is not built (blockwise_fp8_zero_fold_amd/build.py builds it)")
-    w = synth.get("tiny_clip")
-    rank = 1
+    w = synth.get(name)
     ref, tabs = harness.run_sharded_all_ranks(w, ranks=[rank])
     un = harness.run_unsharded(w)
     P = harness.masters(w)
@@ -547,8 +549,13 @@ def test_c_abi_consumer_without_python(tmp_path):
         f32 = [repr(float(np.float32(x))) for x in (hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay,
                                                      hp.max_grad_norm)]  # exact float32 values
         f.write(" ".join(f32) + "\n")
+        f.write(f"{int(hp.loss_scaling)} {float(np.float32(hp.init_scale))!r} {float(np.float32(hp.growth_factor))!r} "
+                f"{float(np.float32(hp.backoff_factor))!r} {int(hp.growth_interval)} {int(hp.scale_rule)}\n")
         for t in range(w.steps):
             f.write(f"{ref[rank][t]['extra']!r}\n")
+    if mode == "graph":
+        assert w.dp == 1 and all(ref[rank][t]["extra"] == 0 for t in range(w.steps))
+        assert any(ref[rank][t]["state"]["found_inf"] for t in range(1, w.steps))
     for p in range(w.n_params):
         P[p].tofile(tmp_path / f"master_{p}.bin")
     for t in range(1, w.steps + 1):
@@ -556,7 +563,8 @@ def test_c_abi_consumer_without_python(tmp_path):
         for p in range(w.n_params):
             G[p].tofile(tmp_path / f"grad_{t}_{p}.bin")
     env = {k: v for k, v in os.environ.items() if k != "PYTHONPATH"}
-    r = subprocess.run([exe, str(tmp_path)], capture_output=True, text=True, timeout=120, env=env)
+    args = [exe, str(tmp_path)] + (["graph"] if mode == "graph" else [])
+    r = subprocess.run(args, capture_output=True, text=True, timeout=120, env=env)
     assert r.returncode == 0, r.stderr
     R = ref[rank][-1]
     n = tabs[rank]["shard_slots"]
@@ -564,9 +572,16 @@ def test_c_abi_consumer_without_python(tmp_path):
     assert got.tobytes() == R["master"].tobytes()
     step, k, found, skipped = open(tmp_path / "out_state.txt").read().split()
     assert int(step) == R["state"]["step"] and float(k) == R["state"]["k"]
+    assert int(found) == R["state"]["found_inf"] and int(skipped) == R["state"]["skipped_total"]
     mask = layout.valid_mask(tabs[rank])
     held = {p: np.zeros(s, bool) for p, s in enumerate(w.shapes)}
     layout.unfold_shard(tabs[rank], mask, held)
     for p in range(w.n_params):
         codes = np.fromfile(tmp_path / f"out_codes_{p}.bin", dtype=np.uint8).reshape(w.shapes[p])
         assert (codes[held[p]] == un[-1]["codes"][p][held[p]]).all()
+        blocks = np.zeros(otable.grid(w.shapes[p]), bool)
+        for e in tabs[rank]["entries"]:
+            if e["param"] == p:
+                blocks[int(e["expert"]), int(e["brow"]), int(e["bcol"])] = True
+        sc = np.fromfile(tmp_path / f"out_scales_{p}.bin", dtype=np.float32).reshape(otable.grid(w.shapes[p]))
+        assert sc[blocks].tobytes() == un[-1]["scales"][p][blocks].tobytes()
