@@ -26,6 +26,8 @@ constexpr int kChunksPerRow = kB / 4;
 constexpr int kSumThreads = 256;
 // XCDs of the part; consecutive workgroups of a launch are dealt to them in turn
 constexpr int kXcds = 8;
+// last-level (Infinity) cache of the part, shared by all XCDs
+constexpr int64_t kLastLevelCacheBytes = 256LL << 20;
 constexpr int kStatParts = FP8Z1_STAT_PARTS;
 static_assert(kB % kStatParts == 0 && (kChunks / kStatParts) % kSumThreads == 0, "part split");
 constexpr int kPartRows = kB / kStatParts;
@@ -104,17 +106,40 @@ __device__ __forceinline__ void st_stream(uint4* p, uint4 x) {
 }
 __device__ __forceinline__ void st_stream(uint32_t* p, uint32_t x) { __builtin_nontemporal_store(x, p); }
 
-// 16-byte accesses at addresses that are only element-aligned (a row of a
-// row-major param whose width is not a multiple of 4).  gfx950 under ROCm runs
-// in unaligned-access mode, so these are single dwordx4 instructions (the
-// compiler emits them for these types); the callers only use them on bytes that
-// lie inside the row segment they own.
+// Accesses to row-major params.  Their pointers come from a device array, so
+// the compiler cannot tell they are global and would emit flat instructions;
+// these helpers go through global-address-space pointers.  A row of a param
+// whose width is not a multiple of 4 starts at an element-aligned address only:
+// gfx950 under ROCm runs in unaligned-access mode, so a 16-byte load at 4-byte
+// alignment is still one dwordx4 instruction; the callers only use it on bytes
+// that lie inside the row segment they own.
 typedef float v4f_a4_t __attribute__((ext_vector_type(4), aligned(4)));
+typedef float v4f_a4_global_t __attribute__((ext_vector_type(4), aligned(4), address_space(1)));
+typedef uint32_t v4u_global_t __attribute__((ext_vector_type(4), address_space(1)));
+typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v2u_a2_global_t __attribute__((ext_vector_type(2), aligned(2), address_space(1)));
 
-__device__ __forceinline__ float4 ld_stream_a4(const float* p) {
-  const v4f_a4_t r = __builtin_nontemporal_load(reinterpret_cast<const v4f_a4_t*>(p));
+// streaming 16-byte load of 4 float32 at 4-byte alignment
+__device__ __forceinline__ float4 ld_global_stream_a4(const float* p) {
+  const v4f_a4_t r = __builtin_nontemporal_load((const v4f_a4_global_t*)(p));
   return make_float4(r.x, r.y, r.z, r.w);
 }
+// the same load, cached (for data read again soon)
+__device__ __forceinline__ float4 ld_global_a4(const float* p) {
+  const v4f_a4_t r = *(const v4f_a4_global_t*)(p);
+  return make_float4(r.x, r.y, r.z, r.w);
+}
+// streaming 8-byte load of 4 bfloat16 at 2-byte alignment
+__device__ __forceinline__ uint2 ld_global_stream_a2x8(const uint16_t* p) {
+  const v2u_t r = __builtin_nontemporal_load((const v2u_a2_global_t*)(p));
+  return make_uint2(r.x, r.y);
+}
+// streaming 16-byte store to a 16-byte aligned address
+__device__ __forceinline__ void st_global_stream(void* p, uint4 x) {
+  const v4u_t r = {x.x, x.y, x.z, x.w};
+  __builtin_nontemporal_store(r, (v4u_global_t*)(p));
+}
+// plain 16-byte accesses at element alignment (partial chunks and rows)
 __device__ __forceinline__ float4 ld_a4(const float* p) {
   float4 r;
   __builtin_memcpy(&r, p, 16);

@@ -31,12 +31,20 @@ struct Src;
 // load; see device_util.h), load1: one element
 template <>
 struct Src<float> {
+  // whole chunk of a full block: one streaming 16-byte global load
+  __device__ static float4 load4_full(const float* p) { return ld_global_stream_a4(p); }
+  __device__ static float4 load4_full_cached(const float* p) { return ld_global_a4(p); }
   __device__ static float4 load4(const float* p) { return ld_a4(p); }
   __device__ static float load1(const float* p) { return *p; }
 };
 template <>
 struct Src<uint16_t> {  // bfloat16 bits
   __device__ static float widen(uint32_t b) { return __uint_as_float(b << 16); }
+  __device__ static float4 load4_full(const uint16_t* p) {
+    const uint2 u = ld_global_stream_a2x8(p);
+    return make_float4(widen(u.x & 0xffffu), widen(u.x >> 16), widen(u.y & 0xffffu), widen(u.y >> 16));
+  }
+  __device__ static float4 load4_full_cached(const uint16_t* p) { return load4(p); }
   __device__ static float4 load4(const uint16_t* p) {
     uint2 u;
     __builtin_memcpy(&u, p, 8);
@@ -48,8 +56,10 @@ struct Src<uint16_t> {  // bfloat16 bits
 // One workgroup per part (kPartRows rows) of a slot.  SUMSQ: also write the
 // part's float64 sum of squares to part_sumsq[slot * kStatParts + part].
 // WRITE = false: statistics only (the partials of a row-major grad that the
-// update reads directly, without a folded copy).
-template <typename T, bool SUMSQ, bool WRITE = true>
+// update reads directly, without a folded copy).  KEEP: plain (cached) loads
+// instead of streaming ones, so that grads which fit in the last-level cache
+// are still there when the update reads them again.
+template <typename T, bool SUMSQ, bool WRITE = true, bool KEEP = false>
 __global__ __launch_bounds__(kFoldThreads) void fold_kernel(const SlotPlan* __restrict__ plan,
                                                             const void* const* __restrict__ srcs,
                                                             float* __restrict__ dst,
@@ -84,7 +94,8 @@ __global__ __launch_bounds__(kFoldThreads) void fold_kernel(const SlotPlan* __re
 #pragma unroll
       for (int k = 0; k < kPartPasses; ++k) {
         const int c = t + kFoldThreads * k;
-        x[k] = Src<T>::load4(src + (r0 + c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow));
+        const T* p = src + (r0 + c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow);
+        x[k] = KEEP ? Src<T>::load4_full_cached(p) : Src<T>::load4_full(p);
       }
     } else {
       // partial block: whole chunks inside the real region load as vectors, the
@@ -138,10 +149,17 @@ hipError_t launch(const SlotPlan* plan, void** srcs, float* dst, double* sumsq, 
 
 }  // namespace
 
-hipError_t launch_grad_sumsq(const SlotPlan* plan, void** grads, double* sumsq, int64_t nslots, hipStream_t stream) {
+hipError_t launch_grad_sumsq(const SlotPlan* plan, void** grads, double* sumsq, int64_t nslots, int64_t valid_elems,
+                             hipStream_t stream) {
   if (nslots == 0) return hipSuccess;
-  hipLaunchKernelGGL((fold_kernel<float, true, false>), dim3(fold_grid(nslots)), dim3(kFoldThreads), 0, stream, plan,
-                     grads, nullptr, sumsq, nslots);
+  // grads that fit in the last-level cache (256 MB on MI355X) stay there for the
+  // update's second read; larger ones stream
+  if (valid_elems * 4 <= kLastLevelCacheBytes)
+    hipLaunchKernelGGL((fold_kernel<float, true, false, true>), dim3(fold_grid(nslots)), dim3(kFoldThreads), 0, stream,
+                       plan, grads, nullptr, sumsq, nslots);
+  else
+    hipLaunchKernelGGL((fold_kernel<float, true, false, false>), dim3(fold_grid(nslots)), dim3(kFoldThreads), 0,
+                       stream, plan, grads, nullptr, sumsq, nslots);
   return hipGetLastError();
 }
 
@@ -177,7 +195,9 @@ extern "C" int fp8z1_fold(const fp8z1_table* ct, const void* const* src, int32_t
   rc = device_ptr_list(t, kRoleFoldSrc, src, &dsrc, stream);
   if (rc) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (!dst) return check_hip(launch_grad_sumsq(t->d_plan, dsrc, slot_sumsq, t->info.shard_slots, st), "fold: launch");
+  if (!dst)
+    return check_hip(launch_grad_sumsq(t->d_plan, dsrc, slot_sumsq, t->info.shard_slots, t->info.valid_elems, st),
+                     "fold: launch");
   hipError_t e = src_dtype == FP8Z1_F32
                      ? launch<float>(t->d_plan, dsrc, dst, slot_sumsq, t->info.shard_slots, st)
                      : launch<uint16_t>(t->d_plan, dsrc, dst, slot_sumsq, t->info.shard_slots, st);

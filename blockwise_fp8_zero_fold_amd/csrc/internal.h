@@ -100,6 +100,7 @@ int check_hip(int hip_status, const char* what);
 namespace fp8z1 {
 // Per-slot float64 sums of squares of row-major FP32 grads (no folded copy),
 // in the same order as the fold's fused statistics.
-hipError_t launch_grad_sumsq(const SlotPlan* plan, void** grads, double* sumsq, int64_t nslots, hipStream_t stream);
+hipError_t launch_grad_sumsq(const SlotPlan* plan, void** grads, double* sumsq, int64_t nslots, int64_t valid_elems,
+                             hipStream_t stream);
 }  // namespace fp8z1
 #endif

@@ -243,12 +243,12 @@ struct GradSrc {
   // the 4 elements of chunk c (all real)
   __device__ __forceinline__ float4 chunk(int c) const {
     if (!ROWMAJOR) return ld_stream(folded + c);
-    return ld_stream_a4(rows + (c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow));
+    return ld_global_stream_a4(rows + (c / kChunksPerRow) * ld + 4 * (c % kChunksPerRow));
   }
   // elements j .. j+3 of row i, those at columns >= vc read as 0
   __device__ __forceinline__ void chunk_masked(int c, int i, int j, int vc, float g[4]) const {
     if (!ROWMAJOR || j + 4 <= vc) {
-      const float4 x = ROWMAJOR ? ld_stream_a4(rows + i * ld + j) : ld_stream(folded + c);
+      const float4 x = ROWMAJOR ? ld_global_stream_a4(rows + i * ld + j) : ld_stream(folded + c);
       g[0] = x.x;
       g[1] = x.y;
       g[2] = x.z;
@@ -470,7 +470,8 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
   double* partial = static_cast<double*>(d_workspace);
   if (stats && !given && !presummed && n > 0) {
     if (grad_rows)
-      rc = check_hip(launch_grad_sumsq(t->d_plan, drows, partial, n, s), "step: statistics launch");
+      rc = check_hip(launch_grad_sumsq(t->d_plan, drows, partial, n, t->info.valid_elems, s),
+                     "step: statistics launch");
     else {
       hipLaunchKernelGGL(sumsq_kernel, dim3(static_cast<unsigned>(n * kStatParts)), dim3(kSumThreads), 0, s,
                          t->d_plan, grad, partial);

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(kUnfThreads) void unfold_rows_e4m3_kernel(const Row
     const uint4 x = m ? funnel16(chunk(k - 1), hi, 16 - m) : hi;
     uint8_t* d = row + x0;  // 16-byte aligned
     if (x0 >= 0 && x0 + 16 <= len) {
-      st_stream(reinterpret_cast<uint4*>(d), x);
+      st_global_stream(d, x);
     } else {
       const uint32_t w[4] = {x.x, x.y, x.z, x.w};
       const int b0 = x0 < 0 ? -x0 : 0, b1 = len - x0 < 16 ? len - x0 : 16;
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kUnfThreads) void unfold_blocks_e4m3_kernel(const S
   if (j + 16 <= vc) {
     // a chunk inside the row: one 16-byte store, at any alignment of the row
     if ((reinterpret_cast<uintptr_t>(row + j) & 15u) == 0)
-      st_stream(reinterpret_cast<uint4*>(row + j), x);
+      st_global_stream(row + j, x);
     else
       st_a1(row + j, x);
   } else {
