@@ -186,6 +186,7 @@ struct UpdateArgs {
   int32_t pow2_scale;
   int64_t nslots;
   int32_t xcd_ranges;  // 1: XCD x takes a contiguous range of slots (grid = whole XCD rounds)
+  int32_t cache_codes;  // 1: plain stores for the codes, 0: streaming stores
 };
 
 // Block scale from the block's amax.  Default: amax / 448 (the largest E4M3
@@ -357,8 +358,16 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
   amax = block_max<kUpdThreads>(amax, red);
   const float scale = block_scale(amax, a.pow2_scale != 0);
   if (full) {
+    // codes of a shard up to about twice the last-level cache: plain (cached)
+    // stores, so that the unfold which follows finds many of them still in the
+    // cache; larger ones stream (each choice measured 2-3 % faster on its side)
+    if (a.cache_codes) {
 #pragma unroll
-    for (int q = 0; q < kUpdPasses; ++q) st_stream(codes + t + kUpdThreads * q, pack_codes(pn[q], scale));
+      for (int q = 0; q < kUpdPasses; ++q) codes[t + kUpdThreads * q] = pack_codes(pn[q], scale);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kUpdPasses; ++q) st_stream(codes + t + kUpdThreads * q, pack_codes(pn[q], scale));
+    }
   } else {
 #pragma unroll
     for (int q = 0; q < kUpdPasses; ++q) {
@@ -506,6 +515,7 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
   ua.eps = hp->eps;
   ua.pow2_scale = hp->scale_rule == FP8Z1_SCALE_POW2 ? 1 : 0;
   ua.nslots = n;
+  ua.cache_codes = n * kBlockElems <= 2 * kLastLevelCacheBytes;
   // Row-major grads whose block row segments do not start on 128-byte lines
   // share a line between neighbouring blocks; giving each XCD a contiguous
   // slot range fetches such a line into one L2 instead of two.  Otherwise the

@@ -24,8 +24,8 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const uint4* __restrict
 
 // the update's pattern: one workgroup per 64 KB slot of each float32 array, 16
 // chunks of 16 bytes per lane, the same order as the update kernel: per chunk
-// read g, p, m, v and write p, m, v; after all chunks write 4 bytes of codes
-// per chunk; all streaming
+// read g, p, m, v and write p, m, v (streaming); after all chunks write 4 bytes
+// of codes per chunk (plain stores, as the update does)
 __global__ __launch_bounds__(256) void probe_update_kernel(const float4* __restrict__ g, float4* __restrict__ p,
                                                            float4* __restrict__ m, float4* __restrict__ v,
                                                            uint32_t* __restrict__ q) {
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void probe_update_kernel(const float4* __restr
     keep[k] = b.x + b.y + b.z + b.w;
   }
 #pragma unroll
-  for (int k = 0; k < kPasses; ++k) st_stream(q + base + threadIdx.x + 256 * k, __float_as_uint(keep[k]));
+  for (int k = 0; k < kPasses; ++k) q[base + threadIdx.x + 256 * k] = __float_as_uint(keep[k]);
 }
 
 }  // namespace
