@@ -24,6 +24,7 @@ same shard.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -291,6 +292,87 @@ def sweep_ranks(w, args) -> int:
     return 0
 
 
+def next_rows(w, args) -> int:
+    """The steps after the shard step, and the scale variant, on the same workload:
+    the unfold of the whole all-gathered FP8 buffer (every rank's codes and scales),
+    dequantization of the row-major codes to BF16 and FP32, and the shard step with
+    power-of-two (E8M0) block scales beside the default rule.  One JSON line."""
+    import torch
+
+    import blockwise_fp8_zero_fold_amd as fz
+    from blockwise_fp8_zero_fold_amd.shard import Shard
+    split = fz.SPLIT_PARAM if w.split == "param" else fz.SPLIT_BLOCK
+    stream = torch.cuda.current_stream()
+
+    def ev_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out = {}
+    # whole gathered buffer: codes and scales of all ranks in rank order
+    tall = fz.fp8z1_build_table(w.shapes, w.dp, fz.ALL_RANKS, split)
+    n_all, valid_all = tall.shard_slots, tall.info["valid_elems"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0)
+    folded = torch.randint(0, 256, (n_all * BLOCK,), dtype=torch.uint8, device="cuda", generator=gen)
+    fsc = torch.rand(n_all, dtype=torch.float32, device="cuda", generator=gen)
+    codes = [torch.empty(s, dtype=torch.uint8, device="cuda") for s in w.shapes]
+    scales = [torch.empty((s[0], -(-s[1] // 128), -(-s[2] // 128)), dtype=torch.float32, device="cuda")
+              for s in w.shapes]
+    ms = ev_ms(lambda: fz.fp8z1_unfold(tall, folded, fz.E4M3, fsc, codes, scales), args.steps)
+    nbytes = 2 * valid_all + SLOT_BYTES_UNFOLD * n_all
+    out["whole_buffer_unfold"] = {"slots": n_all, "valid_elems": valid_all, "ms": ms,
+                                  "gbs_algorithmic": nbytes / (ms * 1e-3) / 1e9,
+                                  "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    print(f"# whole-buffer unfold: {ms:.4f} ms", file=sys.stderr, flush=True)
+    del folded, fsc
+    # dequantization of every param's row-major codes
+    for name, dt, tdt, el in (("dequantize_bf16", fz.BF16, torch.bfloat16, 2), ("dequantize_f32", fz.F32,
+                                                                                 torch.float32, 4)):
+        big = max(int(np.prod(s)) for s in w.shapes)
+        buf = torch.empty(big, dtype=tdt, device="cuda")
+
+        def deq():
+            for p, s in enumerate(w.shapes):
+                fz.fp8z1_dequantize(codes[p], scales[p], s, dt, buf[:int(np.prod(s))].view(s))
+        ms = ev_ms(deq, args.steps)
+        tot = sum(int(np.prod(s)) for s in w.shapes)
+        nbytes = (1 + el) * tot
+        out[name] = {"elems": tot, "ms": ms, "gbs_algorithmic": nbytes / (ms * 1e-3) / 1e9,
+                     "frac_of_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        print(f"# {name}: {ms:.4f} ms", file=sys.stderr, flush=True)
+        del buf
+    tall.free()
+    del codes, scales
+    torch.cuda.empty_cache()
+    # the shard step with each scale rule
+    rank = w.ranks[0]
+    sh = Shard(w.shapes, w.dp, rank, split)
+    held = _held(sh.table.entries())
+    weights = _gen_params(w, held, lambda p, e: synth.master_slab(w, p, e), torch.float32)
+    grads = _gen_params(w, held, lambda p, e: synth.grad_slab(w, p, e, 1), torch.float32)
+    rc = [torch.zeros(s, dtype=torch.uint8, device="cuda") if p in held else None for p, s in enumerate(w.shapes)]
+    rs = [torch.zeros((s[0], -(-s[1] // 128), -(-s[2] // 128)), dtype=torch.float32, device="cuda")
+          if p in held else None for p, s in enumerate(w.shapes)]
+    valid = sh.table.info["valid_elems"]
+    for rule_name, rule in (("amax", 0), ("pow2", 1)):
+        hp = fz.Hparams.make(dataclasses.replace(w.hp, scale_rule=rule))
+        sh.init(hp, weights, fz.F32)
+        ms = ev_ms(lambda: sh.step(hp, grads, rc, rs, fold_on_read=True), args.steps)
+        out[f"step_scale_{rule_name}"] = {"ms": ms, "elems_per_s": valid / (ms * 1e-3)}
+        print(f"# step with {rule_name} scales: {ms:.4f} ms", file=sys.stderr, flush=True)
+    print(json.dumps({"next_rows": out, "workload": w.name, "dp": w.dp, "rank": rank, "steps": args.steps,
+                      "device": _device_info(), "source_hash": _source_hash()}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -305,6 +387,9 @@ def main() -> int:
     ap.add_argument("--unfused-stats", action="store_true", help="separate statistics kernel instead of fold-fused")
     ap.add_argument("--cpu-slots", type=int, default=16384, help="oracle sample size (slots) for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--next-rows", action="store_true",
+                    help="time the whole-buffer unfold, dequantization and the E8M0-scale step on the workload and "
+                         "print one JSON line; not the headline line")
     ap.add_argument("--sweep-ranks", action="store_true",
                     help="time the fold-on-read step on every rank's shard of the workload in turn and print one "
                          "JSON line with per-rank times (min / median / max); not the headline line")
@@ -325,7 +410,7 @@ def main() -> int:
     # The oracle baselines run first, before this process touches the GPU (the
     # parallel one starts worker processes).
     cpu = cpu_par = None
-    if not (args.no_cpu_baseline or args.calibrate_copy or args.sweep_ranks):
+    if not (args.no_cpu_baseline or args.calibrate_copy or args.sweep_ranks or args.next_rows):
         from oracle import table as otable
         n_all = otable.build(w.shapes, w.dp, rank, otable.PARAM if w.split == "param" else otable.BLOCK)["shard_slots"]
         slots = min(args.cpu_slots, n_all)
@@ -360,6 +445,8 @@ def main() -> int:
 
     if args.sweep_ranks:
         return sweep_ranks(w, args)
+    if args.next_rows:
+        return next_rows(w, args)
     split = fz.SPLIT_PARAM if w.split == "param" else fz.SPLIT_BLOCK
     torch.cuda.set_device(0)
     t_setup = time.perf_counter()

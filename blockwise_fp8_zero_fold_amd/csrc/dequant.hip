@@ -31,7 +31,7 @@ __device__ __forceinline__ uint16_t to_bf16(float x) {
   return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// one workgroup per row of one expert; lanes walk the row's columns
+// any alignment: one workgroup per row of one expert; lanes walk the row's columns
 template <bool BF16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes, const float* __restrict__ scales,
                                                       int64_t R, int64_t C, void* __restrict__ out) {
@@ -46,6 +46,67 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
       static_cast<uint16_t*>(out)[row * C + c] = to_bf16(y);
     else
       static_cast<float*>(out)[row * C + c] = y;
+  }
+}
+
+// Rows whose codes and outputs are 16-byte aligned (C a multiple of 16, aligned
+// buffers): a workgroup takes kDqRows rows.  FP32: a lane turns 4 codes into
+// one 16-byte store, so each store instruction of a wave covers 1 KB of
+// contiguous output, and loads 4 such chunks before decoding.  BF16: a lane
+// turns 16 codes (one 16-byte load) into two 16-byte stores (measured faster
+// for this output than 8 codes per lane).  The codes of a chunk lie in one
+// 128-column block, so they share one scale.
+constexpr int kDqRows = 4;
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void dequant_vec_kernel(const uint8_t* __restrict__ codes,
+                                                          const float* __restrict__ scales, int64_t rows, int64_t R,
+                                                          int64_t C, void* __restrict__ out) {
+  constexpr int kPer = BF16 ? 16 : 4;  // codes per lane and chunk (BF16: two 16-byte stores)
+  constexpr int kUnroll = BF16 ? 1 : 4;  // chunks a lane loads before it decodes
+  const int64_t nchunk = C / kPer;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * kDqRows;
+  const int64_t cb = (C + kB - 1) / kB;
+  const int64_t total = min(static_cast<int64_t>(kDqRows), rows - row0) * nchunk;
+  for (int64_t i0 = threadIdx.x; i0 < total; i0 += 256 * kUnroll) {
+    uint4 q[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + 256 * u;
+      q[u] = make_uint4(0u, 0u, 0u, 0u);
+      if (i < total) {
+        const uint8_t* src = codes + (row0 + i / nchunk) * C + kPer * (i % nchunk);
+        if (BF16)
+          q[u] = ld_stream(reinterpret_cast<const uint4*>(src));
+        else
+          q[u].x = *reinterpret_cast<const uint32_t*>(src);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + 256 * u;
+      if (i >= total) break;
+      const int64_t row = row0 + i / nchunk, k = i % nchunk;
+      const int64_t e = row / R, r = row % R;
+      const float sc = scales[(e * ((R + kB - 1) / kB) + r / kB) * cb + (kPer * k) / kB];
+      if (BF16) {
+        const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+        uint32_t h[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+          const uint32_t lo = (w[b >> 1] >> (16 * (b & 1))) & 0xffu, hi = (w[b >> 1] >> (16 * (b & 1) + 8)) & 0xffu;
+          h[b] = to_bf16(e4m3_decode(lo) * sc) | (static_cast<uint32_t>(to_bf16(e4m3_decode(hi) * sc)) << 16);
+        }
+        uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + row * C + kPer * k);
+        st_stream(o, make_uint4(h[0], h[1], h[2], h[3]));
+        st_stream(o + 1, make_uint4(h[4], h[5], h[6], h[7]));
+      } else {
+        const uint32_t x = q[u].x;
+        st_stream(reinterpret_cast<float4*>(static_cast<float*>(out) + row * C + kPer * k),
+                  make_float4(e4m3_decode(x & 0xffu) * sc, e4m3_decode((x >> 8) & 0xffu) * sc,
+                              e4m3_decode((x >> 16) & 0xffu) * sc, e4m3_decode(x >> 24) * sc));
+      }
+    }
   }
 }
 
@@ -65,6 +126,14 @@ extern "C" int fp8z1_dequantize(const uint8_t* codes, const float* scales, int64
   const int64_t rows = E * R;
   if (rows > 0x7fffffff) return set_error(FP8Z1_ESHAPE, "dequantize: more than 2^31 rows");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (C % 16 == 0 && reinterpret_cast<uintptr_t>(codes) % 16 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0) {
+    const unsigned grid = static_cast<unsigned>((rows + kDqRows - 1) / kDqRows);
+    if (out_dtype == FP8Z1_BF16)
+      hipLaunchKernelGGL(dequant_vec_kernel<true>, dim3(grid), dim3(256), 0, s, codes, scales, rows, R, C, out);
+    else
+      hipLaunchKernelGGL(dequant_vec_kernel<false>, dim3(grid), dim3(256), 0, s, codes, scales, rows, R, C, out);
+    return check_hip(hipGetLastError(), "dequantize: launch");
+  }
   if (out_dtype == FP8Z1_BF16)
     hipLaunchKernelGGL(dequant_kernel<true>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, s, codes, scales, R, C,
                        out);

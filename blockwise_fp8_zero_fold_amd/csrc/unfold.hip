@@ -172,6 +172,7 @@ extern "C" int fp8z1_unfold(const fp8z1_table* ct, const void* folded, int32_t d
   if (reinterpret_cast<uintptr_t>(folded) % 16) return set_error(FP8Z1_EINVAL, "unfold: folded must be 16-byte aligned");
   const bool with_scales = scales && dst_scales;
   const size_t el = dtype == FP8Z1_F32 ? 4 : 1;
+  if (t->info.shard_slots * kUnfParts > 0x7fffffffLL) return set_error(FP8Z1_ESHAPE, "unfold: too many slots");
   for (const fp8z1_block& e : t->entries) {
     if (e.param < 0) continue;
     const void* p = dst[e.param];
@@ -203,7 +204,8 @@ extern "C" int fp8z1_unfold(const fp8z1_table* ct, const void* folded, int32_t d
     for (size_t p = 0; p < t->shapes.size() && lines; ++p)
       if (t->held[p]) lines = t->shapes[p].C % 128 == 0 && reinterpret_cast<uintptr_t>(dst[p]) % 128 == 0;
     if (lines)
-      hipLaunchKernelGGL(unfold_blocks_e4m3_kernel, dim3(n * kUnfParts), dim3(kUnfThreads), 0, s, t->d_plan,
+      hipLaunchKernelGGL(unfold_blocks_e4m3_kernel, dim3(static_cast<unsigned>(n * kUnfParts)), dim3(kUnfThreads), 0, s,
+                         t->d_plan,
                          static_cast<const uint8_t*>(folded), ddst, with_scales ? scales : nullptr,
                          reinterpret_cast<float* const*>(dsc));
     else if (t->n_rows > 0)
@@ -211,7 +213,7 @@ extern "C" int fp8z1_unfold(const fp8z1_table* ct, const void* folded, int32_t d
                          t->d_rows, static_cast<const uint8_t*>(folded), ddst, with_scales ? scales : nullptr,
                          reinterpret_cast<float* const*>(dsc));
   } else
-    hipLaunchKernelGGL(unfold_f32_kernel, dim3(n), dim3(kUnfThreads), 0, s, t->d_plan,
+    hipLaunchKernelGGL(unfold_f32_kernel, dim3(static_cast<unsigned>(n)), dim3(kUnfThreads), 0, s, t->d_plan,
                        static_cast<const float*>(folded), ddst, with_scales ? scales : nullptr,
                        reinterpret_cast<float* const*>(dsc));
   return check_hip(hipGetLastError(), "unfold: launch");

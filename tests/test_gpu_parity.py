@@ -423,12 +423,13 @@ def test_all_ranks_gather_and_whole_buffer_unfold(name, split):
         assert gh.bits_equal(dsc[p].cpu().numpy(), U["scales"][p]), (name, split, p)
 
 
-def test_dequantize_every_code():
+@pytest.mark.parametrize("shape", [(2, 200, 300), (3, 130, 400)])
+def test_dequantize_every_code(shape):
     """All 256 codes times random scales (one per 128x128 block): float32 bit-exact
-    against the oracle, bfloat16 equal to torch's RNE cast of the oracle's float32."""
+    against the oracle, bfloat16 equal to torch's RNE cast of the oracle's float32.
+    C = 300 takes the any-alignment kernel, C = 400 the 16-code vector kernel."""
     from oracle import quant as oquant
     rng = np.random.default_rng(17)
-    shape = (2, 200, 300)
     codes = rng.integers(0, 256, size=shape, dtype=np.uint8)
     codes[0, 0, :256] = np.arange(256, dtype=np.uint8)
     scales = (2.0 ** rng.uniform(-20, 20, size=otable.grid(shape))).astype(np.float32)
