@@ -23,8 +23,11 @@
  *   - Argument errors are found before anything is launched; a failed
  *     launch or HIP runtime error returns FP8Z1_EHIP.
  *   - GPU calls are asynchronous on the caller's stream (`stream` is a
- *     hipStream_t; NULL is the default stream).  Only fp8z1_state_read and
- *     the first GPU use of a table synchronize.
+ *     hipStream_t; NULL is the default stream).  Host waits happen only in
+ *     fp8z1_state_read / fp8z1_state_write, at the first GPU use of a table
+ *     (its plan is uploaded), in fp8z1_table_free, and when a call passes
+ *     param pointers that differ from the last call of the same kind (the
+ *     library waits for its previous upload of that pointer list).
  *   - Data buffers are caller-owned device memory.  The library owns the
  *     table handle: its host arrays, and (from the first GPU call that uses
  *     it) one device copy of the table plus small device arrays that hold the
