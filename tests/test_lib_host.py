@@ -153,3 +153,37 @@ def test_workspace_bytes_and_constants_match_header():
         w = synth.get(name)
         t = fz.fp8z1_build_table(w.shapes, w.dp, 0, 0)
         assert fz.fp8z1_step_workspace_bytes(t) == 8 * fz.STAT_PARTS * t.shard_slots
+
+
+def test_concurrent_table_builds_and_error_strings():
+    """Threads building tables and hitting argument errors at the same time: every
+    table equals the oracle's and every error message is the calling thread's own
+    (the detail string is thread-local)."""
+    import threading
+    errors = []
+
+    def worker(seed):
+        try:
+            rng = np.random.default_rng(seed)
+            for i in range(60):
+                n = int(rng.integers(1, 6))
+                shapes = [(int(rng.integers(1, 3)), int(rng.integers(1, 500)), int(rng.integers(1, 500)))
+                          for _ in range(n)]
+                dp = int(rng.integers(1, 6))
+                _cmp(shapes, dp, int(rng.integers(0, dp)), i % 2)
+                bad, expect = ((shapes, 0, 0, 0), "dp must be") if seed % 2 else ((shapes, dp, 0, 7), "split must be")
+                try:
+                    fz.fp8z1_build_table(*bad)
+                    errors.append((seed, "no error"))
+                except fz.Fp8z1Error as e:
+                    if expect not in str(e):
+                        errors.append((seed, str(e)))
+        except Exception as e:  # noqa: BLE001 - report any failure from the thread
+            errors.append((seed, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(s,)) for s in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:5]
