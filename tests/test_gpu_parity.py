@@ -508,6 +508,15 @@ def test_extreme_shapes_and_all_padding_ranks():
     _run_parity(few, fold_on_read=True)
 
 
+def test_thirty_steps_of_loss_scaling_and_clipping():
+    """30 steps: the loss scale doubles every 2 clean steps and halves on the injected
+    overflow, clipping stays active; every rank's state and folded buffers stay equal
+    to the oracle's bit for bit after every step, on both routes."""
+    w = synth.get("tiny_lossscale").with_(name="tiny_lossscale_30", steps=30)
+    _run_parity(w)
+    _run_parity(w, fold_on_read=True)
+
+
 @pytest.mark.parametrize("seed", range(8))
 def test_random_shape_sets(seed):
     """Random sets of 1-5 params (E 1-3, R and C 1-400, so most rows start off any
