@@ -591,8 +591,12 @@ def main() -> int:
 
     probe_bufs = [torch.zeros(nslots * BLOCK, dtype=torch.float32, device="cuda") for _ in range(4)]
     probe_codes = torch.zeros(nslots * BLOCK, dtype=torch.uint8, device="cuda")
-    t_pat = ev_time(lambda: fz.fp8z1_probe_update_pattern(*probe_bufs, probe_codes, nslots), 10)
     pat_bytes = 29 * nslots * BLOCK
+    pat_gbs = {}
+    for parts in (1, 2, 4, 8):  # 64, 32, 16, 8 KB of each array per workgroup
+        t = ev_time(lambda: fz.fp8z1_probe_update_pattern(*probe_bufs, probe_codes, nslots, parts), 10)
+        pat_gbs[f"{64 // parts}KB"] = pat_bytes / t / 1e9
+    t_pat = pat_bytes / (pat_gbs["64KB"] * 1e9)
     t_copy = ev_time(lambda: fz.fp8z1_probe_copy(probe_bufs[0], probe_bufs[1]), 10)
     copy_bytes = 2 * probe_bufs[0].numel() * 4
     # the same copy with the workgroups in flight spread over S far-apart ranges
@@ -603,7 +607,8 @@ def main() -> int:
             spread_gbs[S] = copy_bytes / ev_time(lambda: fz.fp8z1_probe_copy(probe_bufs[0], probe_bufs[1], S), 10) / 1e9
     del probe_bufs, probe_codes
     torch.cuda.empty_cache()
-    ceiling = {"update_pattern_gbs": pat_bytes / t_pat / 1e9, "copy_gbs": copy_bytes / t_copy / 1e9,
+    ceiling = {"update_pattern_gbs": pat_bytes / t_pat / 1e9, "update_pattern_gbs_by_tile": pat_gbs,
+               "update_pattern_best_gbs": max(pat_gbs.values()), "copy_gbs": copy_bytes / t_copy / 1e9,
                "update_vs_pattern": achieved / (pat_bytes / t_pat / 1e9),
                "copy_gbs_by_spread": spread_gbs,
                "note": "same-run streaming references: fp8z1_probe_update_pattern (the update's loads and stores, "

@@ -106,7 +106,7 @@ _sig = {
     "fp8z1_encode_e4m3": (C.c_int, [_vp, _vp, C.c_int64, _vp]),
     "fp8z1_dequantize": (C.c_int, [_vp, _vp, C.c_int64, C.c_int64, C.c_int64, C.c_int32, _vp, _vp]),
     "fp8z1_probe_copy": (C.c_int, [_vp, _vp, C.c_int64, C.c_int64, _vp]),
-    "fp8z1_probe_update_pattern": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int64, _vp]),
+    "fp8z1_probe_update_pattern": (C.c_int, [_vp, _vp, _vp, _vp, _vp, C.c_int64, C.c_int32, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(lib, _name)
@@ -353,9 +353,9 @@ def fp8z1_probe_copy(src, dst, spread: int = 1, stream=None) -> None:
     _check(lib.fp8z1_probe_copy(_ptr(src), _ptr(dst), n, spread, _stream(stream)), "fp8z1_probe_copy")
 
 
-def fp8z1_probe_update_pattern(g, p, m, v, codes, nslots: int, stream=None) -> None:
+def fp8z1_probe_update_pattern(g, p, m, v, codes, nslots: int, parts: int = 1, stream=None) -> None:
     for name, x in (("g", g), ("p", p), ("m", m), ("v", v)):
         _need(x, nslots * 16384 * 4, f"probe_update_pattern {name}")
     _need(codes, nslots * 16384, "probe_update_pattern codes")
-    _check(lib.fp8z1_probe_update_pattern(_ptr(g), _ptr(p), _ptr(m), _ptr(v), _ptr(codes), nslots, _stream(stream)),
-           "fp8z1_probe_update_pattern")
+    _check(lib.fp8z1_probe_update_pattern(_ptr(g), _ptr(p), _ptr(m), _ptr(v), _ptr(codes), nslots, parts,
+                                          _stream(stream)), "fp8z1_probe_update_pattern")

@@ -22,15 +22,19 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const uint4* __restrict
   st_stream(dst + i, ld_stream(src + i));
 }
 
-// the update's pattern: one workgroup per 64 KB slot of each float32 array, 16
-// chunks of 16 bytes per lane, the same order as the update kernel: per chunk
-// read g, p, m, v and write p, m, v (streaming); after all chunks write 4 bytes
-// of codes per chunk (plain stores, as the update does)
+// the update's pattern: one workgroup per 1/PARTS of a slot (64 KB / PARTS of
+// each float32 array), 16 / PARTS chunks of 16 bytes per lane, the same order
+// as the update kernel: per chunk read g, p, m, v and write p, m, v
+// (streaming); after all chunks write 4 bytes of codes per chunk (plain
+// stores, as the update does).  PARTS = 1 is the update's own tiling; smaller
+// tiles show what the same mix of streams reaches when each workgroup owns
+// less memory.
+template <int PARTS>
 __global__ __launch_bounds__(256) void probe_update_kernel(const float4* __restrict__ g, float4* __restrict__ p,
                                                            float4* __restrict__ m, float4* __restrict__ v,
                                                            uint32_t* __restrict__ q) {
-  constexpr int kPasses = kChunks / 256;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * kChunks;
+  constexpr int kPasses = kChunks / 256 / PARTS;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * (kChunks / PARTS);
   float keep[kPasses];
 #pragma unroll
   for (int k = 0; k < kPasses; ++k) {
@@ -66,18 +70,25 @@ extern "C" int fp8z1_probe_copy(const void* src, void* dst, int64_t bytes, int64
 }
 
 extern "C" int fp8z1_probe_update_pattern(const float* g, float* p, float* m, float* v, uint8_t* codes, int64_t nslots,
-                                          void* stream) {
+                                          int32_t parts, void* stream) {
   if (!g || !p || !m || !v || !codes || nslots < 0)
     return set_error(FP8Z1_EINVAL, "probe_update_pattern: NULL argument");
+  if (parts != 1 && parts != 2 && parts != 4 && parts != 8)
+    return set_error(FP8Z1_EINVAL, "probe_update_pattern: parts must be 1, 2, 4 or 8");
   const void* ptrs[5] = {g, p, m, v, codes};
   for (const void* q : ptrs)
     if (reinterpret_cast<uintptr_t>(q) % 16)
       return set_error(FP8Z1_EINVAL, "probe_update_pattern: buffers must be 16-byte aligned");
   if (nslots == 0) return FP8Z1_OK;
-  if (nslots > 0x7fffffff) return set_error(FP8Z1_EINVAL, "probe_update_pattern: too large");
-  hipLaunchKernelGGL(probe_update_kernel, dim3(static_cast<unsigned>(nslots)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), reinterpret_cast<const float4*>(g),
-                     reinterpret_cast<float4*>(p), reinterpret_cast<float4*>(m), reinterpret_cast<float4*>(v),
-                     reinterpret_cast<uint32_t*>(codes));
+  if (nslots * parts > 0x7fffffff) return set_error(FP8Z1_EINVAL, "probe_update_pattern: too large");
+  const dim3 grid(static_cast<unsigned>(nslots * parts));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  float4 *p4 = reinterpret_cast<float4*>(p), *m4 = reinterpret_cast<float4*>(m), *v4 = reinterpret_cast<float4*>(v);
+  uint32_t* q = reinterpret_cast<uint32_t*>(codes);
+  if (parts == 1) hipLaunchKernelGGL(probe_update_kernel<1>, grid, dim3(256), 0, s, g4, p4, m4, v4, q);
+  if (parts == 2) hipLaunchKernelGGL(probe_update_kernel<2>, grid, dim3(256), 0, s, g4, p4, m4, v4, q);
+  if (parts == 4) hipLaunchKernelGGL(probe_update_kernel<4>, grid, dim3(256), 0, s, g4, p4, m4, v4, q);
+  if (parts == 8) hipLaunchKernelGGL(probe_update_kernel<8>, grid, dim3(256), 0, s, g4, p4, m4, v4, q);
   return check_hip(hipGetLastError(), "probe_update_pattern: launch");
 }

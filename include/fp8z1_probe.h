@@ -27,11 +27,14 @@ extern "C" {
 int fp8z1_probe_copy(const void* src, void* dst, int64_t bytes, int64_t spread, void* stream);
 
 /* The update kernel's traffic over nslots 128x128 slots: per slot, read 64 KB
- * of each of g, p, m, v and write 64 KB of each of p, m, v plus 16 KB of
- * codes, one workgroup per slot, 16-byte streaming accesses.  g, p, m, v are
- * nslots*16384 float32, codes nslots*16384 bytes, all 16-byte aligned. */
+ * of each of g, p, m, v and write 64 KB of each of p, m, v (16-byte streaming
+ * accesses) plus 16 KB of codes (plain 4-byte stores).  parts = 1: one
+ * workgroup per slot, the update's own tiling; parts = 2, 4 or 8: one
+ * workgroup per 1/parts of a slot, the same streams with less memory per
+ * workgroup.  g, p, m, v are nslots*16384 float32, codes nslots*16384 bytes,
+ * all 16-byte aligned. */
 int fp8z1_probe_update_pattern(const float* g, float* p, float* m, float* v, uint8_t* codes, int64_t nslots,
-                               void* stream);
+                               int32_t parts, void* stream);
 
 #ifdef __cplusplus
 }

@@ -187,3 +187,10 @@ def test_concurrent_table_builds_and_error_strings():
     for t in threads:
         t.join()
     assert not errors, errors[:5]
+
+
+def test_probe_argument_errors():
+    with pytest.raises(fz.Fp8z1Error, match="parts must be"):
+        fz.fp8z1_probe_update_pattern(16, 16, 16, 16, 16, 4, parts=3, stream=0)
+    assert fz.lib.fp8z1_probe_copy(16, 16, 100, 1, None) == -1  # FP8Z1_EINVAL: not a multiple of 4096
+    assert "multiple of 4096" in fz.lib.fp8z1_last_error().decode()
