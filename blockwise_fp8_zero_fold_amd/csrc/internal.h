@@ -78,6 +78,11 @@ struct fp8z1_table {
   fp8z1::SlotPlan* d_plan = nullptr;
   fp8z1::RowItem* d_rows = nullptr;  // unfold work items
   int64_t n_rows = 0;
+  // slot lists of the update: full blocks, and the rest (partial blocks and
+  // padding slots); both empty when every slot is a full block
+  int32_t* d_full_slots = nullptr;
+  int32_t* d_other_slots = nullptr;
+  int64_t n_full_slots = 0, n_other_slots = 0;
   std::vector<char> held;  // per param: the table holds a block of it
   fp8z1::PtrCache ptrs[fp8z1::kNumRoles];
 };

@@ -91,6 +91,14 @@ int ensure_device(fp8z1_table* t, void* stream) {
     s = s1;
   }
   if (rows.size() > 0x7fffffffULL) return set_error(FP8Z1_ESHAPE, "table: too many unfold work items");
+  // update slot lists: full blocks apart from the rest, so that the update's
+  // full-block kernel carries no partial-block code
+  std::vector<int32_t> full_slots, other_slots;
+  for (size_t s = 0; s < n; ++s) {
+    const fp8z1_block& e = t->entries[s];
+    (e.param >= 0 && e.vrows == kB && e.vcols == kB ? full_slots : other_slots).push_back(static_cast<int32_t>(s));
+  }
+  if (other_slots.empty()) full_slots.clear();  // all full: the update runs over the slots in order
   // (a failed earlier attempt may have left some of these allocated: keep them)
   for (int r = 0; r < kNumRoles; ++r) {
     PtrCache& c = t->ptrs[r];
@@ -121,6 +129,17 @@ int ensure_device(fp8z1_table* t, void* stream) {
     if (rc) return rc;
   }
   t->n_rows = static_cast<int64_t>(rows.size());
+  for (int which = 0; which < 2; ++which) {
+    std::vector<int32_t>& list = which ? other_slots : full_slots;
+    int32_t*& dst = which ? t->d_other_slots : t->d_full_slots;
+    if (list.empty()) continue;
+    if (!dst) rc = check_hip(hipMalloc(reinterpret_cast<void**>(&dst), list.size() * sizeof(int32_t)), "hipMalloc(slots)");
+    if (rc) return rc;
+    rc = check_hip(hipMemcpy(dst, list.data(), list.size() * sizeof(int32_t), hipMemcpyHostToDevice), "hipMemcpy(slots)");
+    if (rc) return rc;
+  }
+  t->n_full_slots = static_cast<int64_t>(full_slots.size());
+  t->n_other_slots = static_cast<int64_t>(other_slots.size());
   t->device = dev;
   return FP8Z1_OK;
 }
@@ -157,7 +176,7 @@ using namespace fp8z1;
 
 extern "C" void fp8z1_table_free(fp8z1_table* t) {
   if (!t) return;
-  bool any = t->d_plan != nullptr || t->d_rows != nullptr;
+  bool any = t->d_plan != nullptr || t->d_rows != nullptr || t->d_full_slots != nullptr || t->d_other_slots != nullptr;
   for (int r = 0; r < kNumRoles; ++r) any = any || t->ptrs[r].host || t->ptrs[r].dev || t->ptrs[r].done;
   if (any) {  // device resources exist only after a GPU call used the table
     int cur = -1;
@@ -175,6 +194,8 @@ extern "C" void fp8z1_table_free(fp8z1_table* t) {
     }
     if (t->d_plan) (void)hipFree(t->d_plan);
     if (t->d_rows) (void)hipFree(t->d_rows);
+    if (t->d_full_slots) (void)hipFree(t->d_full_slots);
+    if (t->d_other_slots) (void)hipFree(t->d_other_slots);
     if (t->device >= 0 && cur >= 0 && cur != t->device) (void)hipSetDevice(cur);
   }
   delete t;
