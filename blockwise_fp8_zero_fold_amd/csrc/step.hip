@@ -95,15 +95,35 @@ struct FinalizeArgs {
   int32_t extra_found_inf;
 };
 
-constexpr int kFinThreads = 256;
+constexpr int kFinThreads = 1024;
+constexpr int kFinAcc = 8;  // independent accumulators per lane (loads in flight)
 
 // Level 2 of the sum of squares: the shard's partials (one per quarter slot)
-// summed in a fixed order -- lane i takes partials i, i + 256, ... in
-// increasing order, then the block reduction.  Every lane gets the total.
+// summed in a fixed order.  Partial i goes to lane i % 1024, accumulator
+// (i / 1024) % 8 of that lane, each accumulator adding its partials in
+// increasing order; a lane adds its 8 accumulators in order, then the block
+// reduction combines the lanes.  (One dependent chain of loads per lane made
+// this a latency-bound 0.25 ms for the 229,376 partials of the full step.)
 __device__ __forceinline__ double sum_partials(const double* __restrict__ partial, int64_t count, double* red) {
-  double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < count; i += kFinThreads) acc += partial[i];
-  return block_sum<kFinThreads>(acc, red);
+  double acc[kFinAcc];
+#pragma unroll
+  for (int u = 0; u < kFinAcc; ++u) acc[u] = 0.0;
+  int64_t i = threadIdx.x;
+  for (; i + (kFinAcc - 1) * kFinThreads < count; i += kFinAcc * kFinThreads) {
+    double x[kFinAcc];
+#pragma unroll
+    for (int u = 0; u < kFinAcc; ++u) x[u] = partial[i + u * kFinThreads];
+#pragma unroll
+    for (int u = 0; u < kFinAcc; ++u) acc[u] += x[u];
+  }
+  // the last partial round: fewer than kFinAcc partials left for this lane
+#pragma unroll
+  for (int u = 0; u < kFinAcc - 1; ++u)
+    if (i + u * kFinThreads < count) acc[u] += partial[i + u * kFinThreads];
+  double tot = acc[0];
+#pragma unroll
+  for (int u = 1; u < kFinAcc; ++u) tot += acc[u];
+  return block_sum<kFinThreads>(tot, red);
 }
 
 __global__ __launch_bounds__(kFinThreads) void shard_sumsq_kernel(const double* __restrict__ partial, int64_t count,
