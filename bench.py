@@ -92,12 +92,18 @@ def _held(entries):
 
 
 def _source_hash() -> str:
+    """Hash of the kernel sources with comments and blank space taken out, so
+    that it changes when the code does and not when only its comments do."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "blockwise_fp8_zero_fold_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
+            text = open(os.path.join(csrc, f), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
             h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -11,8 +11,8 @@
 // Kernels, all on the caller's stream, no host synchronization:
 //   K1 sumsq_kernel   one workgroup per quarter slot: float64 sum of squares
 //                     of its real grads -> workspace[4 * slot + part] (level 1)
-//   K2 finalize_kernel one workgroup: fixed-order float64 sum of the part
-//                     sums + the other ranks' sum -> overflow flag, clip and
+//   K2 finalize_kernel one workgroup of 1024 lanes: fixed-order float64 sum
+//                     of the part sums + the other ranks' sum -> overflow flag, clip and
 //                     unscale factor k, bias-correction scalars, loss scale;
 //                     written to the device state                (level 2)
 //   K3 update_kernel  one workgroup per slot: AdamW on g, p, m, v (16-byte
