@@ -43,7 +43,9 @@ __device__ __forceinline__ uint4 funnel16(const uint4 lo, const uint4 hi, int sh
 // that cover it.  Lane chunk k of a row starting m bytes past a 16-byte
 // boundary takes run bytes [16k - m, 16k - m + 16): the folded row segments
 // of the run's blocks are 128-byte runs, so those bytes are the tail of run
-// chunk k - 1 and the head of run chunk k, joined with a funnel shift.
+// chunk k - 1 and the head of run chunk k, joined with a funnel shift.  A
+// lane loads only chunk k and takes chunk k - 1 from the previous lane (a
+// shuffle; the first lane of a wave and the first chunk of a row load it).
 // Chunks wholly inside the row are one aligned (streaming) store; the first
 // and last chunk of a row are written byte by byte, only the row's own bytes,
 // so no byte outside the run is ever written.
@@ -76,7 +78,15 @@ __global__ __launch_bounds__(kUnfThreads) void unfold_rows_e4m3_kernel(const Row
                                                       16 * (q & 7)));
     };
     const uint4 hi = chunk(k);
-    const uint4 x = m ? funnel16(chunk(k - 1), hi, 16 - m) : hi;
+    // chunk k - 1 of the row is the previous lane's chunk, unless this lane
+    // starts a wave or a row
+    uint4 prev;
+    prev.x = __shfl_up(hi.x, 1);
+    prev.y = __shfl_up(hi.y, 1);
+    prev.z = __shfl_up(hi.z, 1);
+    prev.w = __shfl_up(hi.w, 1);
+    const bool from_lane = (threadIdx.x & 63) != 0 && k > 0;
+    const uint4 x = m ? funnel16(from_lane ? prev : chunk(k - 1), hi, 16 - m) : hi;
     uint8_t* d = row + x0;  // 16-byte aligned
     if (x0 >= 0 && x0 + 16 <= len) {
       st_global_stream(d, x);
