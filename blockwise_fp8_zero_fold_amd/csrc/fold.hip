@@ -6,11 +6,12 @@
 // swaps the block-column index with the row-within-block index, so each
 // 128-element row segment of the source moves whole to a contiguous 512-byte
 // destination.  The kernel is therefore a segment gather, not a transpose:
-// four workgroups per slot (32 rows each), 32 lanes per row segment, 16-byte
-// loads (at any element alignment of the source rows) and 16-byte stores; in a
-// partial block only the chunk across the last real column is loaded element
-// by element.  Every source byte is read once, every destination byte
-// written once.
+// four workgroups per slot (32 rows each; XCD x takes a contiguous range of
+// them), 32 lanes per row segment, 16-byte loads (at any element alignment of
+// the source rows) and 16-byte stores; in a partial block only the chunk
+// across the last real column is loaded element by element.  Every source
+// byte is read once, every destination byte written once.  The same kernel
+// without stores is the statistics pass over row-major grads.
 #include <hip/hip_runtime.h>
 
 #include "device_util.h"

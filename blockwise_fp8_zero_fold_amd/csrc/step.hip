@@ -19,8 +19,12 @@
 //                     streaming loads and stores), the updated block kept in
 //                     registers, block amax (wave shuffles + LDS), scale,
 //                     E4M3 codes.  Returns at once when K2 flagged a skip.
+//                     Launched once over the full-block slots (a build with
+//                     no partial-block code) and once over the partial blocks
+//                     and padding slots, or once over all slots when every
+//                     slot is a full block.
 // K1 is left out when no statistics are needed, or when the fold already
-// wrote the per-slot sums (fused statistics).
+// wrote the per-quarter sums (fused statistics).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
