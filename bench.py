@@ -514,6 +514,8 @@ def main() -> int:
         sh.unfold(codes, scales)
         rec("unfold", 1)
 
+    medians = {}
+
     def timed(mode):
         for _ in range(args.warmup):
             one_step(mode)
@@ -527,7 +529,9 @@ def main() -> int:
             one_step(mode, ev, i)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        ms = {k: float(np.mean([a.elapsed_time(b) for a, b in zip(*ev[k])])) for k in ev}
+        times = {k: [a.elapsed_time(b) for a, b in zip(*ev[k])] for k in ev}
+        ms = {k: float(np.mean(v)) for k, v in times.items()}
+        medians[mode] = {k: float(np.median(v)) for k, v in times.items()}
         print(f"# {mode}: {args.steps} steps in {elapsed:.3f}s; per call ms: {ms}", file=sys.stderr, flush=True)
         return elapsed * 1e3 / args.steps, ms
 
@@ -559,6 +563,7 @@ def main() -> int:
 
     modes = [args.mode, "fold" if args.mode == "fold_on_read" else "fold_on_read"]
     results = {m: timed(m) for m in modes}
+    headline_medians = dict(medians[args.mode])  # before the skipped-step timing reuses the route
     graph_ms = graph_timed(args.mode)
 
     skip = None
@@ -650,6 +655,7 @@ def main() -> int:
         "gbs_algorithmic": total_bytes / (ms_per_step * 1e-3) / 1e9,
         "hbm_frac_step": total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "per_call_ms": ms,
+        "per_call_ms_median": headline_medians,
         "roofline": {
             "kernel": "update_kernel" + ("<rowmajor>" if args.mode == "fold_on_read" else "<folded>")
                       + " + finalize_kernel" + (" + statistics pass" if stats and (args.mode == "fold_on_read" or not fused) else ""),
