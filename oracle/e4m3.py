@@ -30,7 +30,8 @@ def encode(x: np.ndarray) -> np.ndarray:
     """float32 array -> uint8 E4M3 codes, elementwise."""
     x = np.asarray(x, dtype=np.float32)
     sign = ((x.view(np.uint32) >> np.uint32(31)).astype(np.uint8)) << np.uint8(7)
-    a = np.abs(x.astype(np.float64))
+    with np.errstate(invalid="ignore"):  # signalling NaNs widen to quiet NaNs, flagged below
+        a = np.abs(x.astype(np.float64))
     nan = np.isnan(a)
     sat = ~nan & (a >= MAX)
     fin = ~nan & ~sat
