@@ -499,8 +499,12 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
     return set_error(FP8Z1_EINVAL, std::string(who) + ": betas must be in [0, 1)");
   if (!(hp->eps > 0.0f) || !std::isfinite(hp->lr) || !std::isfinite(hp->weight_decay))
     return set_error(FP8Z1_EINVAL, std::string(who) + ": eps must be > 0, lr and weight_decay finite");
+  if (std::isnan(hp->max_grad_norm)) return set_error(FP8Z1_EINVAL, std::string(who) + ": max_grad_norm is NaN");
   if (hp->loss_scaling && hp->growth_interval < 1)
     return set_error(FP8Z1_EINVAL, std::string(who) + ": growth_interval must be >= 1");
+  if (hp->loss_scaling && !(hp->growth_factor > 0.0f && std::isfinite(hp->growth_factor) &&
+                            hp->backoff_factor > 0.0f && std::isfinite(hp->backoff_factor)))
+    return set_error(FP8Z1_EINVAL, std::string(who) + ": growth_factor and backoff_factor must be finite and > 0");
   if (hp->scale_rule != FP8Z1_SCALE_AMAX && hp->scale_rule != FP8Z1_SCALE_POW2)
     return set_error(FP8Z1_EINVAL, std::string(who) + ": scale_rule must be FP8Z1_SCALE_AMAX or FP8Z1_SCALE_POW2");
   if (grad_rows) {

@@ -125,11 +125,12 @@ typedef struct {
  * once to float32. */
 typedef struct {
   float lr, beta1, beta2, eps, weight_decay;
-  float max_grad_norm;     /* <= 0: no clipping */
+  float max_grad_norm;     /* <= 0: no clipping; NaN is rejected (FP8Z1_EINVAL) */
   int32_t loss_scaling;    /* 0: off (S = 1) */
   float init_scale;        /* loss scale S at fp8z1_state_init */
   float growth_factor;     /* S *= growth_factor after growth_interval clean steps */
-  float backoff_factor;    /* S *= backoff_factor on overflow */
+  float backoff_factor;    /* S *= backoff_factor on overflow; with loss_scaling on, both
+                              factors must be finite and > 0 (else FP8Z1_EINVAL) */
   int32_t growth_interval;
   int32_t extra_found_inf; /* overflow flag of the other ranks (the all-reduced flag) */
   int32_t scale_rule;      /* FP8Z1_SCALE_AMAX (0) or FP8Z1_SCALE_POW2 (1) */

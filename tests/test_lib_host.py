@@ -118,6 +118,14 @@ def test_argument_errors_before_any_gpu_work():
     hp_bad = fz.Hparams.make(synth.Hparams(beta1=1.0))
     with pytest.raises(fz.Fp8z1Error, match="betas"):
         fz.fp8z1_step(t, hp_bad, 16, 16, 16, 16, 16, 16, 16, stream=0)
+    hp_nan = fz.Hparams.make(synth.Hparams(max_grad_norm=float("nan")))
+    with pytest.raises(fz.Fp8z1Error, match="max_grad_norm is NaN"):
+        fz.fp8z1_step(t, hp_nan, 16, 16, 16, 16, 16, 16, 16, workspace=16, stream=0)
+    for bad in (dict(growth_factor=0.0), dict(backoff_factor=-0.5), dict(growth_factor=float("inf")),
+                dict(backoff_factor=float("nan"))):
+        hp_ls = fz.Hparams.make(synth.Hparams(loss_scaling=True, **bad))
+        with pytest.raises(fz.Fp8z1Error, match="growth_factor and backoff_factor"):
+            fz.fp8z1_step_rowmajor(t, hp_ls, 16, [16], 16, 16, 16, 16, 16, workspace=16, stream=0)
     with pytest.raises(fz.Fp8z1Error, match="NULL or misaligned"):
         fz.fp8z1_step_rowmajor(t, hp, 16, [None], 16, 16, 16, 16, 16, stream=0)
     with pytest.raises(fz.Fp8z1Error, match="NULL or misaligned"):
