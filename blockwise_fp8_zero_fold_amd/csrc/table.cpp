@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstring>
 #include <new>
+#include <stdexcept>
 #include <numeric>
 
 #include "internal.h"
@@ -167,6 +168,9 @@ extern "C" int fp8z1_build_table(const fp8z1_shape* shapes, int32_t n_params, in
   } catch (const std::bad_alloc&) {
     delete t;
     return set_error(FP8Z1_ENOMEM, "build_table: host allocation failed");
+  } catch (const std::length_error&) {  // more entries than a vector can hold
+    delete t;
+    return set_error(FP8Z1_ENOMEM, "build_table: table too large for host memory");
   }
 
   int64_t valid = 0;
