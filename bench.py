@@ -621,6 +621,9 @@ def main() -> int:
     ceiling = {"update_pattern_gbs": pat_bytes / t_pat / 1e9, "update_pattern_gbs_by_tile": pat_gbs,
                "update_pattern_best_gbs": max(pat_gbs.values()), "copy_gbs": copy_bytes / t_copy / 1e9,
                "update_vs_pattern": achieved / (pat_bytes / t_pat / 1e9),
+               "update_vs_best_pattern": achieved / max(pat_gbs.values()),
+               # the second denominator beside the 8 TB/s peak: a plain device copy in the same run
+               "update_vs_copy": achieved / (copy_bytes / t_copy / 1e9),
                "copy_gbs_by_spread": spread_gbs,
                "note": "same-run streaming references: fp8z1_probe_update_pattern (the update's loads and stores, "
                        "no arithmetic, same slot count) and fp8z1_probe_copy (plain copy, 4 KB per workgroup)"}

@@ -39,3 +39,5 @@ def test_bench_line_has_the_contract_fields():
         assert key in rl, key
     assert rl["bound"] == "hbm" and rl["peak"] == 8000.0 and rl["unit"] == "GB/s"
     assert abs(rl["frac"] - rl["achieved"] / rl["peak"]) < 1e-12
+    c = d["ceiling"]  # the same-run copy ceiling, the second denominator
+    assert c["copy_gbs"] > 0 and abs(c["update_vs_copy"] - rl["achieved"] / c["copy_gbs"]) < 1e-9
