@@ -18,6 +18,23 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout.strip() == ""
 
 
+def test_cpu_baseline_legs_time_the_oracle():
+    """The bench's host baselines run the oracle on the CPU: on a bounded slot sample in
+    this process, and over contiguous slot ranges in fresh worker processes; both count
+    the real elements of the slots they cover (rank 1 of the tiny set holds the whole
+    [200, 300] param: 60,000 real elements in 6 slots)."""
+    import bench
+    import synth
+    w = synth.get("tiny")
+    rate, valid, dt = bench.cpu_baseline(w, 1, 6, steps=1)
+    assert valid == 200 * 300 and dt > 0 and rate == pytest.approx(valid / dt)
+    rate_p, valid_p, dt_p, used = bench.cpu_baseline_parallel(w, 1, 6, 2, steps=1)
+    assert used == 2 and valid_p == 200 * 300 and rate_p == pytest.approx(valid_p / dt_p)
+    # a sample starting mid-shard: slots 3..5 of rank 1 (block row 1 of [200, 300]: 72 rows)
+    _, valid_tail, _ = bench.cpu_baseline(w, 1, 3, steps=1, first=3)
+    assert valid_tail == 72 * 300
+
+
 @pytest.mark.gpu
 def test_bench_line_has_the_contract_fields():
     torch = pytest.importorskip("torch")
