@@ -44,15 +44,23 @@ def test_decode_every_code():
     assert back.tolist() == codes[fin].tolist()
 
 
+SUB = 1 << 18  # compared in pieces that stay in cache: ~10x faster than whole chunks
+
+
 def _torch_chunk(i):
     import torch
     torch.set_num_threads(1)
-    u = np.arange(i * CHUNK, (i + 1) * CHUNK, dtype=np.uint64).astype(np.uint32)
-    x = u.view(np.float32)
-    ref = torch.from_numpy(x).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    got = e4m3.encode(x)
-    bad = np.nonzero(ref != got)[0]
-    return i, len(bad), (int(u[bad[0]]) if len(bad) else None)
+    nbad, first = 0, None
+    for lo in range(i * CHUNK, (i + 1) * CHUNK, SUB):
+        u = np.arange(lo, lo + SUB, dtype=np.uint64).astype(np.uint32)
+        x = u.view(np.float32)
+        ref = torch.from_numpy(x).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got = e4m3.encode(x)
+        bad = np.nonzero(ref != got)[0]
+        if len(bad) and first is None:
+            first = int(u[bad[0]])
+        nbad += len(bad)
+    return i, nbad, first
 
 
 def test_exhaustive_vs_torch_cast():
