@@ -218,7 +218,9 @@ def _table_info(w, rank: int) -> dict:
 
 
 def _device_info() -> dict:
-    """What identifies the GPU and its memory set-up (bandwidth differs between parts)."""
+    """What identifies the GPU and its memory set-up (bandwidth differs between parts):
+    torch's device properties, and from the GPU's own sysfs node (matched by PCI
+    address) the current clock levels, partition modes, VBIOS, VRAM vendor and power cap."""
     import glob
 
     import torch
@@ -228,22 +230,60 @@ def _device_info() -> dict:
     uuid = getattr(pr, "uuid", None)
     if uuid is not None:
         info["uuid"] = str(uuid)
-    for key in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):  # the current level is marked '*'
-        for f in sorted(glob.glob(f"/sys/class/drm/card*/device/{key}")):
-            try:
-                cur = [ln.split(":", 1)[1].strip(" *\n") for ln in open(f) if ln.rstrip().endswith("*")]
+    pci = None
+    if all(hasattr(pr, a) for a in ("pci_domain_id", "pci_bus_id", "pci_device_id")):
+        pci = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+        info["pci"] = pci
+    cards = sorted(glob.glob("/sys/class/drm/card*/device"))
+    dev = None
+    for c in cards:
+        try:
+            if pci and os.path.realpath(c).endswith(pci):
+                dev = c
+                break
+        except OSError:
+            pass
+    if dev is None and cards:
+        dev = cards[0]
+        info["sysfs_node"] = "first card (no PCI match)"
+
+    def read(name):
+        try:
+            return open(os.path.join(dev, name)).read().strip()
+        except (OSError, TypeError):
+            return None
+
+    if dev is not None:
+        for key in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk", "pp_dpm_socclk"):  # current level marked '*'
+            text = read(key)
+            if text:
+                cur = [ln.split(":", 1)[1].strip(" *") for ln in text.splitlines() if ln.rstrip().endswith("*")]
                 if cur:
                     info[key.replace("pp_dpm_", "clock_")] = cur[0]
-                    break
-            except (OSError, IndexError):
-                pass
-    for key in ("current_memory_partition", "current_compute_partition"):
-        for f in sorted(glob.glob(f"/sys/class/drm/card*/device/{key}")):
+        for key in ("current_memory_partition", "current_compute_partition", "vbios_version",
+                    "mem_info_vram_vendor"):
+            v = read(key)
+            if v:
+                info[key] = v
+        for f in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_cap"))):
             try:
-                info[key] = open(f).read().strip()
+                info["power_cap_w"] = int(open(f).read().strip()) / 1e6
                 break
-            except OSError:
+            except (OSError, ValueError):
                 pass
+        # temperatures (edge / junction / memory) and power right after the timed work
+        for f in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", "temp*_input"))):
+            try:
+                label = open(f.replace("_input", "_label")).read().strip()
+                info[f"temp_{label}_c"] = int(open(f).read().strip()) / 1000
+            except (OSError, ValueError):
+                pass
+        for name in ("power1_average", "power1_input"):
+            for f in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*", name))):
+                try:
+                    info["power_w"] = int(open(f).read().strip()) / 1e6
+                except (OSError, ValueError):
+                    pass
     return info
 
 
