@@ -91,6 +91,21 @@ def _held(entries):
     return {p: sorted(s) for p, s in held.items()}
 
 
+def _update_kernel_names(entries, mode: str) -> str:
+    """The update kernels fp8z1_step* launches on this shard: the 1024-lane full-block
+    kernel over the full blocks when there are at least 8,192 of them, the general
+    kernel over the rest (partial blocks, padding slots, or a small shard)."""
+    g = "<rowmajor>" if mode == "fold_on_read" else "<folded>"
+    full = int(((entries["vrows"] == 128) & (entries["vcols"] == 128) & (entries["param"] >= 0)).sum())
+    other = len(entries) - full
+    names = []
+    if full >= 8192:
+        names.append("update_full_kernel" + g)
+    if other or full < 8192:
+        names.append("update_kernel" + g)
+    return " + ".join(names)
+
+
 def _source_hash() -> str:
     """Hash of the kernel sources with comments and blank space taken out, so
     that it changes when the code does and not when only its comments do."""
@@ -700,7 +715,7 @@ def main() -> int:
         "per_call_ms": ms,
         "per_call_ms_median": headline_medians,
         "roofline": {
-            "kernel": "update_kernel" + ("<rowmajor>" if args.mode == "fold_on_read" else "<folded>")
+            "kernel": _update_kernel_names(sh.table.entries(), args.mode)
                       + " + finalize_kernel" + (" + statistics pass" if stats and (args.mode == "fold_on_read" or not fused) else ""),
             "bound": "hbm",
             "achieved": achieved,

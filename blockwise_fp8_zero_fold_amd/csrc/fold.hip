@@ -196,11 +196,13 @@ extern "C" int fp8z1_fold(const fp8z1_table* ct, const void* const* src, int32_t
   rc = device_ptr_list(t, kRoleFoldSrc, src, &dsrc, stream);
   if (rc) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
   if (!dst)
-    return check_hip(launch_grad_sumsq(t->d_plan, dsrc, slot_sumsq, t->info.shard_slots, t->info.valid_elems, st),
-                     "fold: launch");
-  hipError_t e = src_dtype == FP8Z1_F32
-                     ? launch<float>(t->d_plan, dsrc, dst, slot_sumsq, t->info.shard_slots, st)
-                     : launch<uint16_t>(t->d_plan, dsrc, dst, slot_sumsq, t->info.shard_slots, st);
-  return check_hip(e, "fold: launch");
+    e = launch_grad_sumsq(t->d_plan, dsrc, slot_sumsq, t->info.shard_slots, t->info.valid_elems, st);
+  else if (src_dtype == FP8Z1_F32)
+    e = launch<float>(t->d_plan, dsrc, dst, slot_sumsq, t->info.shard_slots, st);
+  else
+    e = launch<uint16_t>(t->d_plan, dsrc, dst, slot_sumsq, t->info.shard_slots, st);
+  rc = check_hip(e, "fold: launch");
+  return rc ? rc : note_use(t, stream);
 }

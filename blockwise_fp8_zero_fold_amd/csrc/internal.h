@@ -55,7 +55,17 @@ static_assert(sizeof(RowItem) == 48, "RowItem is 48 bytes");
 // and as many of their rows as fit about kRowItemBytes bytes of FP8 output.
 constexpr int kRowItemBytes = 16384;
 
-enum PtrRole { kRoleFoldSrc = 0, kRoleUnfoldDst = 1, kRoleUnfoldScale = 2, kRoleStepGrad = 3, kNumRoles = 4 };
+// One pointer list per kind of call, so that a call of one kind cannot retarget a
+// captured graph of another kind (the FP8 and the FP32 unfold have their own).
+enum PtrRole {
+  kRoleFoldSrc = 0,
+  kRoleUnfoldDst = 1,
+  kRoleUnfoldScale = 2,
+  kRoleStepGrad = 3,
+  kRoleUnfoldDstF32 = 4,
+  kRoleUnfoldScaleF32 = 5,
+  kNumRoles = 6
+};
 
 // Device-side pointer list for one role: a pinned host mirror, the device
 // array and an event marking the end of the last upload from the mirror.
@@ -85,6 +95,11 @@ struct fp8z1_table {
   int64_t n_full_slots = 0, n_other_slots = 0;
   std::vector<char> held;  // per param: the table holds a block of it
   fp8z1::PtrCache ptrs[fp8z1::kNumRoles];
+  // recorded on the caller's stream after the launches of every uncaptured
+  // call that uses the table's device arrays; release waits for it (calls on
+  // one table are on one stream or ordered by the caller, so the last one
+  // finishing means all have)
+  void* last_use = nullptr;  // hipEvent_t
 };
 
 namespace fp8z1 {
@@ -97,6 +112,8 @@ int ensure_device(fp8z1_table* t, void* stream);
 // array.  A change is refused while `stream` is being captured.
 int device_ptr_list(fp8z1_table* t, PtrRole role, const void* const* host_list, void*** out, void* stream);
 int check_hip(int hip_status, const char* what);
+// Record the table's last-use event on `stream` (nothing inside a capture).
+int note_use(fp8z1_table* t, void* stream);
 
 }  // namespace fp8z1
 

@@ -112,6 +112,11 @@ int ensure_device(fp8z1_table* t, void* stream) {
     if (rc) return rc;
     c.valid = false;
   }
+  if (!t->last_use) {
+    rc = check_hip(hipEventCreateWithFlags(reinterpret_cast<hipEvent_t*>(&t->last_use), hipEventDisableTiming),
+                   "hipEventCreate");
+    if (rc) return rc;
+  }
   if (n) {
     if (!t->d_plan)
       rc = check_hip(hipMalloc(reinterpret_cast<void**>(&t->d_plan), n * sizeof(SlotPlan)), "hipMalloc(plan)");
@@ -142,6 +147,14 @@ int ensure_device(fp8z1_table* t, void* stream) {
   t->n_other_slots = static_cast<int64_t>(other_slots.size());
   t->device = dev;
   return FP8Z1_OK;
+}
+
+int note_use(fp8z1_table* t, void* stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  int rc = check_hip(hipStreamIsCapturing(static_cast<hipStream_t>(stream), &st), "hipStreamIsCapturing");
+  if (rc || st != hipStreamCaptureStatusNone || !t->last_use) return rc;
+  return check_hip(hipEventRecord(static_cast<hipEvent_t>(t->last_use), static_cast<hipStream_t>(stream)),
+                   "hipEventRecord(table use)");
 }
 
 int device_ptr_list(fp8z1_table* t, PtrRole role, const void* const* host_list, void*** out, void* stream) {
@@ -176,16 +189,21 @@ using namespace fp8z1;
 
 extern "C" void fp8z1_table_free(fp8z1_table* t) {
   if (!t) return;
-  bool any = t->d_plan != nullptr || t->d_rows != nullptr || t->d_full_slots != nullptr || t->d_other_slots != nullptr;
+  bool any = t->d_plan != nullptr || t->d_rows != nullptr || t->d_full_slots != nullptr ||
+             t->d_other_slots != nullptr || t->last_use != nullptr;
   for (int r = 0; r < kNumRoles; ++r) any = any || t->ptrs[r].host || t->ptrs[r].dev || t->ptrs[r].done;
   if (any) {  // device resources exist only after a GPU call used the table
     int cur = -1;
     (void)hipGetDevice(&cur);
     if (t->device >= 0 && cur != t->device) (void)hipSetDevice(t->device);
-    // pending uploads and kernels that use the table must have finished
+    // pending uploads and the kernels of the table's last call must have
+    // finished (only this table's own work is waited for)
     for (int r = 0; r < kNumRoles; ++r)
       if (t->ptrs[r].done) (void)hipEventSynchronize(static_cast<hipEvent_t>(t->ptrs[r].done));
-    (void)hipDeviceSynchronize();
+    if (t->last_use) {
+      (void)hipEventSynchronize(static_cast<hipEvent_t>(t->last_use));
+      (void)hipEventDestroy(static_cast<hipEvent_t>(t->last_use));
+    }
     for (int r = 0; r < kNumRoles; ++r) {
       PtrCache& c = t->ptrs[r];
       if (c.host) (void)hipHostFree(c.host);

@@ -15,14 +15,15 @@
 //                     of the part sums + the other ranks' sum -> overflow flag, clip and
 //                     unscale factor k, bias-correction scalars, loss scale;
 //                     written to the device state                (level 2)
-//   K3 update_kernel  one workgroup per slot: AdamW on g, p, m, v (16-byte
+//   K3 update          one workgroup per slot: AdamW on g, p, m, v (16-byte
 //                     streaming loads and stores), the updated block kept in
 //                     registers, block amax (wave shuffles + LDS), scale,
 //                     E4M3 codes.  Returns at once when K2 flagged a skip.
-//                     Launched once over the full-block slots (a build with
-//                     no partial-block code) and once over the partial blocks
-//                     and padding slots, or once over all slots when every
-//                     slot is a full block.
+//                     update_full_kernel (1024 lanes) takes the full-block
+//                     slots: it issues every load of its block before any
+//                     arithmetic and every store after it; update_kernel
+//                     (512 lanes) takes partial blocks and padding slots, and
+//                     every slot of a small shard.
 // K1 is left out when no statistics are needed, or when the fold already
 // wrote the per-quarter sums (fused statistics).
 #include <hip/hip_runtime.h>
@@ -209,7 +210,6 @@ struct UpdateArgs {
   float beta1, beta2, one_minus_beta1, one_minus_beta2, eps;
   int32_t pow2_scale;
   int64_t nslots;
-  int32_t xcd_ranges;  // 1: XCD x takes a contiguous range of slots (grid = whole XCD rounds)
   int32_t cache_codes;  // 1: plain stores for the codes, 0: streaming stores
 };
 
@@ -229,9 +229,6 @@ __device__ __forceinline__ float block_scale(float amax, bool pow2) {
   const int x = max(k - 8, -127);
   return x >= -126 ? __uint_as_float(static_cast<uint32_t>(x + 127) << 23) : __uint_as_float(1u << (x + 149));
 }
-
-constexpr int kUpdThreads = 512;
-constexpr int kUpdPasses = kChunks / kUpdThreads;
 
 struct Moments {
   float p, m, v;
@@ -277,10 +274,124 @@ struct GradSrc {
   }
 };
 
-// FULL: every slot of the launch is a full block (no partial-block or padding
-// code is compiled in).  slots: the launch's slot list, NULL for slots
-// 0 .. nslots-1 in order.
-template <bool ROWMAJOR, bool FULL>
+// Pointers of one slot's g, p, m, v and codes.
+template <bool ROWMAJOR>
+struct SlotPtrs {
+  GradSrc<ROWMAJOR> g;
+  float4 *p, *m, *v;
+  uint32_t* codes;
+};
+
+template <bool ROWMAJOR>
+__device__ __forceinline__ SlotPtrs<ROWMAJOR> slot_ptrs(const SlotPlan& P, int64_t s, const float* grad,
+                                                       void* const* grad_rows, float* master, float* mom1,
+                                                       float* mom2, uint8_t* fp8) {
+  SlotPtrs<ROWMAJOR> r;
+  const int64_t base = s * (kBlockElems / 4);
+  if (ROWMAJOR) {
+    r.g.folded = nullptr;
+    r.g.rows = P.param >= 0 ? static_cast<const float*>(grad_rows[P.param]) + P.off : nullptr;
+    r.g.ld = P.ld;
+  } else {
+    r.g.folded = reinterpret_cast<const float4*>(grad) + base;
+    r.g.rows = nullptr;
+    r.g.ld = 0;
+  }
+  r.p = reinterpret_cast<float4*>(master) + base;
+  r.m = reinterpret_cast<float4*>(mom1) + base;
+  r.v = reinterpret_cast<float4*>(mom2) + base;
+  r.codes = reinterpret_cast<uint32_t*>(fp8 + s * kBlockElems);
+  return r;
+}
+
+// Slot of workgroup b: entry b of the launch's slot list, or slot b.  The
+// plain order keeps the workgroups in flight on one compact window of slots
+// (giving each XCD a contiguous range of slots instead ran the ragged shard's
+// update 6 % slower, the MoE shard's 10 %).
+__device__ __forceinline__ int64_t launch_slot(const int32_t* slots) {
+  const int64_t b = blockIdx.x;
+  return slots ? slots[b] : b;
+}
+
+// Full blocks.  1024 lanes, each with 4 chunks (16 elements) of the block: all
+// 16 loads of a lane (g, then p, m, v) are issued before any arithmetic, and
+// the stores of p, m and v follow the arithmetic as one group; the scheduling
+// barriers keep the compiler from interleaving them.  The workgroup so asks for
+// its whole block (4 x 64 KB) at once, and one workgroup per CU (97 VGPRs) is
+// in flight: on the MoE shard this ran 10 % faster than 512 lanes with loads
+// and stores interleaved per chunk (two workgroups per CU), and faster than
+// the same with 512 lanes (its 32 loads per lane leave one workgroup of 8
+// waves per CU) or with the next slot's loads overlapping the current slot's
+// stores in a persistent grid.
+constexpr int kFullThreads = 1024;
+constexpr int kFullPasses = kChunks / kFullThreads;
+
+template <bool ROWMAJOR>
+__global__ __launch_bounds__(kFullThreads) void update_full_kernel(
+    const SlotPlan* __restrict__ plan, const fp8z1_state* __restrict__ st, const float* __restrict__ grad,
+    void* const* __restrict__ grad_rows, float* __restrict__ master, float* __restrict__ mom1,
+    float* __restrict__ mom2, uint8_t* __restrict__ fp8, float* __restrict__ scales, UpdateArgs a,
+    const int32_t* __restrict__ slots) {
+  __shared__ float red[kFullThreads / 64];
+  if (st->found_inf) return;  // skipped step: nothing changes
+  const float k = st->k, decay = st->decay, step_size = st->step_size, bc2 = st->bc2_sqrt;
+  const int64_t s = launch_slot(slots);
+  const SlotPlan P = plan[s];
+  const SlotPtrs<ROWMAJOR> X = slot_ptrs<ROWMAJOR>(P, s, grad, grad_rows, master, mom1, mom2, fp8);
+  const int t = threadIdx.x;
+  float4 g[kFullPasses], p[kFullPasses], m[kFullPasses], v[kFullPasses];
+#pragma unroll
+  for (int q = 0; q < kFullPasses; ++q) g[q] = X.g.chunk(t + kFullThreads * q);
+#pragma unroll
+  for (int q = 0; q < kFullPasses; ++q) p[q] = ld_stream(X.p + t + kFullThreads * q);
+#pragma unroll
+  for (int q = 0; q < kFullPasses; ++q) m[q] = ld_stream(X.m + t + kFullThreads * q);
+#pragma unroll
+  for (int q = 0; q < kFullPasses; ++q) v[q] = ld_stream(X.v + t + kFullThreads * q);
+  __builtin_amdgcn_sched_barrier(0);
+  float amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kFullPasses; ++q) {
+    const Moments e0 = adamw1(g[q].x, p[q].x, m[q].x, v[q].x, k, decay, step_size, bc2, a);
+    const Moments e1 = adamw1(g[q].y, p[q].y, m[q].y, v[q].y, k, decay, step_size, bc2, a);
+    const Moments e2 = adamw1(g[q].z, p[q].z, m[q].z, v[q].z, k, decay, step_size, bc2, a);
+    const Moments e3 = adamw1(g[q].w, p[q].w, m[q].w, v[q].w, k, decay, step_size, bc2, a);
+    p[q] = make_float4(e0.p, e1.p, e2.p, e3.p);
+    m[q] = make_float4(e0.m, e1.m, e2.m, e3.m);
+    v[q] = make_float4(e0.v, e1.v, e2.v, e3.v);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e0.p), fabsf(e1.p)), fmaxf(fabsf(e2.p), fabsf(e3.p))));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < kFullPasses; ++q) st_stream(X.p + t + kFullThreads * q, p[q]);
+#pragma unroll
+  for (int q = 0; q < kFullPasses; ++q) st_stream(X.m + t + kFullThreads * q, m[q]);
+#pragma unroll
+  for (int q = 0; q < kFullPasses; ++q) st_stream(X.v + t + kFullThreads * q, v[q]);
+  __builtin_amdgcn_sched_barrier(0);
+  amax = block_max<kFullThreads>(amax, red);
+  const float scale = block_scale(amax, a.pow2_scale != 0);
+  // codes of a shard up to about twice the last-level cache: plain (cached)
+  // stores, so that the unfold which follows finds many of them still in the
+  // cache; larger ones stream
+  if (a.cache_codes) {
+#pragma unroll
+    for (int q = 0; q < kFullPasses; ++q) X.codes[t + kFullThreads * q] = pack_codes(p[q], scale);
+  } else {
+#pragma unroll
+    for (int q = 0; q < kFullPasses; ++q) st_stream(X.codes + t + kFullThreads * q, pack_codes(p[q], scale));
+  }
+  if (t == 0) scales[s] = scale;
+}
+
+// Any slot: full blocks, partial blocks and padding slots.  512 lanes, 8
+// chunks per lane, loads and stores per chunk (68 VGPRs, several workgroups
+// per CU: on a small shard, or on the few partial blocks of a large one, the
+// full-block kernel's one workgroup per CU leaves too few rounds).
+constexpr int kUpdThreads = 512;
+constexpr int kUpdPasses = kChunks / kUpdThreads;
+
+template <bool ROWMAJOR>
 __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __restrict__ plan,
                                                              const fp8z1_state* __restrict__ st,
                                                              const float* __restrict__ grad,
@@ -292,70 +403,27 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
   __shared__ float red[kUpdThreads / 64];
   if (st->found_inf) return;  // skipped step: nothing changes
   const float k = st->k, decay = st->decay, step_size = st->step_size, bc2 = st->bc2_sqrt;
-
-  int64_t b = blockIdx.x;
-  if (a.xcd_ranges) {
-    b = (blockIdx.x % kXcds) * (static_cast<int64_t>(gridDim.x) / kXcds) + blockIdx.x / kXcds;
-    if (b >= a.nslots) return;  // whole workgroup
-  }
-  const int64_t s = slots ? slots[b] : b;
+  const int64_t s = launch_slot(slots);
   const SlotPlan P = plan[s];
   const int t = threadIdx.x;
-  uint32_t* codes = reinterpret_cast<uint32_t*>(fp8 + s * kBlockElems);
-  if (!FULL && P.param < 0) {
+  const SlotPtrs<ROWMAJOR> X = slot_ptrs<ROWMAJOR>(P, s, grad, grad_rows, master, mom1, mom2, fp8);
+  uint32_t* codes = X.codes;
+  if (P.param < 0) {
 #pragma unroll
     for (int q = 0; q < kUpdPasses; ++q) codes[t + kUpdThreads * q] = 0u;
     if (t == 0) scales[s] = 1.0f;
     return;
   }
-  const int64_t base = s * (kBlockElems / 4);
-  GradSrc<ROWMAJOR> G;
-  if (ROWMAJOR) {
-    G.folded = nullptr;
-    G.rows = static_cast<const float*>(grad_rows[P.param]) + P.off;
-    G.ld = P.ld;
-  } else {
-    G.folded = reinterpret_cast<const float4*>(grad) + base;
-    G.rows = nullptr;
-    G.ld = 0;
-  }
-  float4* p4 = reinterpret_cast<float4*>(master) + base;
-  float4* m4 = reinterpret_cast<float4*>(mom1) + base;
-  float4* v4 = reinterpret_cast<float4*>(mom2) + base;
+  const GradSrc<ROWMAJOR>& G = X.g;
+  float4* p4 = X.p;
+  float4* m4 = X.m;
+  float4* v4 = X.v;
 
   float4 pn[kUpdPasses];
   float amax = 0.0f;
   const int vr = P.vr, vc = P.vc;
-  const bool full = FULL || (vr == kB && vc == kB);
-  if (FULL && !ROWMAJOR) {
-    // folded grads, full blocks: read and compute every pass first, keeping the
-    // new p, m, v in registers, then write them, so that the workgroup's reads
-    // and writes come in two phases (measured 7 % faster than writing each
-    // pass as it is done; fewer, longer-lived workgroups are in flight).  For
-    // row-major grads the compiler's own schedule of the loop below already
-    // holds most stores back and was faster than this form.
-    float4 mn[kUpdPasses], vn[kUpdPasses];
-#pragma unroll
-    for (int q = 0; q < kUpdPasses; ++q) {
-      const int c = t + kUpdThreads * q;
-      const float4 g = G.chunk(c), p = ld_stream(p4 + c), m = ld_stream(m4 + c), v = ld_stream(v4 + c);
-      const Moments e0 = adamw1(g.x, p.x, m.x, v.x, k, decay, step_size, bc2, a);
-      const Moments e1 = adamw1(g.y, p.y, m.y, v.y, k, decay, step_size, bc2, a);
-      const Moments e2 = adamw1(g.z, p.z, m.z, v.z, k, decay, step_size, bc2, a);
-      const Moments e3 = adamw1(g.w, p.w, m.w, v.w, k, decay, step_size, bc2, a);
-      pn[q] = make_float4(e0.p, e1.p, e2.p, e3.p);
-      mn[q] = make_float4(e0.m, e1.m, e2.m, e3.m);
-      vn[q] = make_float4(e0.v, e1.v, e2.v, e3.v);
-      amax = fmaxf(amax, fmaxf(fmaxf(fabsf(e0.p), fabsf(e1.p)), fmaxf(fabsf(e2.p), fabsf(e3.p))));
-    }
-#pragma unroll
-    for (int q = 0; q < kUpdPasses; ++q) {
-      const int c = t + kUpdThreads * q;
-      st_stream(p4 + c, pn[q]);
-      st_stream(m4 + c, mn[q]);
-      st_stream(v4 + c, vn[q]);
-    }
-  } else if (full) {
+  const bool full = vr == kB && vc == kB;
+  if (full) {
 #pragma unroll
     for (int q = 0; q < kUpdPasses; ++q) {
       const int c = t + kUpdThreads * q;
@@ -416,9 +484,6 @@ __global__ __launch_bounds__(kUpdThreads) void update_kernel(const SlotPlan* __r
   amax = block_max<kUpdThreads>(amax, red);
   const float scale = block_scale(amax, a.pow2_scale != 0);
   if (full) {
-    // codes of a shard up to about twice the last-level cache: plain (cached)
-    // stores, so that the unfold which follows finds many of them still in the
-    // cache; larger ones stream (each choice measured 2-3 % faster on its side)
     if (a.cache_codes) {
 #pragma unroll
       for (int q = 0; q < kUpdPasses; ++q) codes[t + kUpdThreads * q] = pack_codes(pn[q], scale);
@@ -568,7 +633,7 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(kFinThreads), 0, s, partial, d_state, fa);
   rc = check_hip(hipGetLastError(), "step: finalize launch");
   if (rc) return rc;
-  if (n == 0) return FP8Z1_OK;
+  if (n == 0) return note_use(t, stream);
   UpdateArgs ua;
   ua.beta1 = hp->beta1;
   ua.beta2 = hp->beta2;
@@ -577,38 +642,29 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
   ua.eps = hp->eps;
   ua.pow2_scale = hp->scale_rule == FP8Z1_SCALE_POW2 ? 1 : 0;
   ua.cache_codes = n * kBlockElems <= 2 * kLastLevelCacheBytes;
-  // Row-major grads whose block row segments do not start on 128-byte lines
-  // share a line between neighbouring blocks; giving each XCD a contiguous
-  // slot range fetches such a line into one L2 instead of two.  Otherwise the
-  // plain order keeps the workgroups in flight on one compact window.
-  ua.xcd_ranges = 0;
-  if (grad_rows)
-    for (size_t p = 0; p < t->shapes.size() && !ua.xcd_ranges; ++p)
-      if (t->held[p])
-        ua.xcd_ranges = t->shapes[p].C % 32 != 0 || reinterpret_cast<uintptr_t>(grad_rows[p]) % 128 != 0;
   // full blocks first (all slots in order when every slot is one), then the
-  // partial blocks and padding slots.  The full-block kernels hold one or two
-  // workgroups per CU; below kManyFullSlots slots that leaves too few rounds
-  // (the dense shard: 3,440 slots ran 2-7 % slower), so small launches take the
-  // general kernel, which holds more.
+  // partial blocks and padding slots.  The full-block kernel holds one
+  // workgroup per CU; below kManyFullSlots slots that leaves few rounds, and
+  // small launches take the general kernel, which holds several (on the dense
+  // shard's 3,440 slots the two ran within 0.5 % of each other).
   constexpr int64_t kManyFullSlots = 8192;
   auto launch = [&](bool full, const int32_t* list, int64_t count) {
     if (count == 0) return;
     full = full && count >= kManyFullSlots;
     ua.nslots = count;
-    const unsigned grid = static_cast<unsigned>(ua.xcd_ranges ? (count + kXcds - 1) / kXcds * kXcds : count);
+    const unsigned grid = static_cast<unsigned>(count);
     if (grad_rows && full)
-      hipLaunchKernelGGL((update_kernel<true, true>), dim3(grid), dim3(kUpdThreads), 0, s, t->d_plan, d_state, nullptr,
+      hipLaunchKernelGGL(update_full_kernel<true>, dim3(grid), dim3(kFullThreads), 0, s, t->d_plan, d_state, nullptr,
                          drows, master, m, v, fp8, scales, ua, list);
     else if (grad_rows)
-      hipLaunchKernelGGL((update_kernel<true, false>), dim3(grid), dim3(kUpdThreads), 0, s, t->d_plan, d_state,
-                         nullptr, drows, master, m, v, fp8, scales, ua, list);
+      hipLaunchKernelGGL(update_kernel<true>, dim3(grid), dim3(kUpdThreads), 0, s, t->d_plan, d_state, nullptr, drows,
+                         master, m, v, fp8, scales, ua, list);
     else if (full)
-      hipLaunchKernelGGL((update_kernel<false, true>), dim3(grid), dim3(kUpdThreads), 0, s, t->d_plan, d_state, grad,
+      hipLaunchKernelGGL(update_full_kernel<false>, dim3(grid), dim3(kFullThreads), 0, s, t->d_plan, d_state, grad,
                          nullptr, master, m, v, fp8, scales, ua, list);
     else
-      hipLaunchKernelGGL((update_kernel<false, false>), dim3(grid), dim3(kUpdThreads), 0, s, t->d_plan, d_state,
-                         grad, nullptr, master, m, v, fp8, scales, ua, list);
+      hipLaunchKernelGGL(update_kernel<false>, dim3(grid), dim3(kUpdThreads), 0, s, t->d_plan, d_state, grad, nullptr,
+                         master, m, v, fp8, scales, ua, list);
   };
   if (t->n_other_slots == 0) {
     launch(true, nullptr, n);
@@ -618,7 +674,8 @@ int step_impl(fp8z1_table* t, const fp8z1_hparams* hp, fp8z1_state* d_state, con
     if (rc) return rc;
     launch(false, t->d_other_slots, t->n_other_slots);
   }
-  return check_hip(hipGetLastError(), "step: update launch");
+  rc = check_hip(hipGetLastError(), "step: update launch");
+  return rc ? rc : note_use(t, stream);
 }
 
 }  // namespace

@@ -196,11 +196,13 @@ extern "C" int fp8z1_unfold(const fp8z1_table* ct, const void* folded, int32_t d
   int rc = ensure_device(t, stream);
   if (rc) return rc;
   void** ddst = nullptr;
-  rc = device_ptr_list(t, kRoleUnfoldDst, const_cast<const void* const*>(dst), &ddst, stream);
+  const bool f32 = dtype == FP8Z1_F32;
+  rc = device_ptr_list(t, f32 ? kRoleUnfoldDstF32 : kRoleUnfoldDst, const_cast<const void* const*>(dst), &ddst, stream);
   if (rc) return rc;
   void** dsc = nullptr;
   if (with_scales) {
-    rc = device_ptr_list(t, kRoleUnfoldScale, reinterpret_cast<const void* const*>(dst_scales), &dsc, stream);
+    rc = device_ptr_list(t, f32 ? kRoleUnfoldScaleF32 : kRoleUnfoldScale,
+                         reinterpret_cast<const void* const*>(dst_scales), &dsc, stream);
     if (rc) return rc;
   }
   const int64_t n = t->info.shard_slots;
@@ -226,5 +228,6 @@ extern "C" int fp8z1_unfold(const fp8z1_table* ct, const void* folded, int32_t d
     hipLaunchKernelGGL(unfold_f32_kernel, dim3(static_cast<unsigned>(n)), dim3(kUnfThreads), 0, s, t->d_plan,
                        static_cast<const float*>(folded), ddst, with_scales ? scales : nullptr,
                        reinterpret_cast<float* const*>(dsc));
-  return check_hip(hipGetLastError(), "unfold: launch");
+  rc = check_hip(hipGetLastError(), "unfold: launch");
+  return rc ? rc : note_use(t, stream);
 }

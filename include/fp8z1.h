@@ -36,7 +36,10 @@
  *   - A table is bound to the device current at its first GPU use.  All GPU
  *     calls that use one table must be issued on one stream, or ordered by
  *     the caller; calls on distinct tables are independent and thread-safe.
- *     fp8z1_table_free waits for the device to finish before releasing.
+ *     fp8z1_table_free waits for the table's own pending work (the pointer
+ *     list uploads and the kernels of its last uncaptured call) before
+ *     releasing, not for the whole device; replays of a captured graph that
+ *     uses the table must have finished before it is freed.
  *   - Graph capture: fp8z1_fold, fp8z1_step, fp8z1_step_rowmajor,
  *     fp8z1_unfold, fp8z1_state_init and fp8z1_dequantize only launch
  *     kernels once a table is set up on the device and its pointer lists
@@ -45,9 +48,12 @@
  *     capture.  A captured call that would need set-up (first device use of
  *     the table, or param pointers that differ from the last call of the
  *     same kind) returns FP8Z1_EINVAL instead.  A replayed graph reads the
- *     table's current pointer lists: a later uncaptured call with other
- *     param pointers retargets it, so keep them fixed while the graph is in
- *     use.  fp8z1_state_read/state_write synchronize and cannot be captured.
+ *     table's current pointer lists: a later uncaptured call of the same
+ *     kind with other param pointers retargets it, so keep them fixed while
+ *     the graph is in use.  Each kind of call has its own lists (fold
+ *     sources, step grads, FP8 unfold destinations and scales, FP32 unfold
+ *     destinations and scales), so a call of one kind never retargets
+ *     another kind's graph.  fp8z1_state_read/state_write synchronize and cannot be captured.
  *   - Rows of row-major arrays may start at any element alignment: kernels
  *     use 16-byte accesses (gfx950 runs in unaligned-access mode) but never
  *     touch a byte outside the block row segment they own.

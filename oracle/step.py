@@ -17,7 +17,7 @@ against each other over all ranks.
 """
 from __future__ import annotations
 
-from typing import Dict, Tuple
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 
@@ -28,12 +28,19 @@ from .table import B, grid
 
 def step_sharded(tab: dict, hp, state: dict, grad: np.ndarray, master: np.ndarray, m: np.ndarray,
                  v: np.ndarray, codes: np.ndarray, scales: np.ndarray,
-                 extra_sumsq: float = 0.0, extra_found_inf: bool = False):
+                 extra_sumsq: float = 0.0, extra_found_inf: bool = False, k: Optional[float] = None):
     """One step on a folded shard ([slots,128,128] float32 grad/master/m/v, uint8 codes,
-    float32 scales[slots]).  Returns (state, master, m, v, codes, scales) as new arrays."""
+    float32 scales[slots]).  Returns (state, master, m, v, codes, scales) as new arrays.
+
+    ``k``, when given, replaces the clip-and-unscale factor the finalize derives from
+    the sum of squares ([DS-ZeRO] section 7).  The float64 sum is the one result of the
+    step that depends on a reduction order; another order may round k to a neighbouring
+    float32, and the rest of the step is then checked with that k."""
     mask = valid_mask(tab)
     local = optim.local_sumsq(grad[mask]) if optim.stats_needed(hp) else None
     st = optim.finalize(state, hp, local, extra_sumsq, extra_found_inf)
+    if k is not None and not st["found_inf"]:
+        st["k"] = float(np.float32(k))
     master, m, v, codes, scales = (a.copy() for a in (master, m, v, codes, scales))
     if st["found_inf"]:
         return st, master, m, v, codes, scales

@@ -199,6 +199,70 @@ SMALL_WORKLOADS = {
 }
 
 
+# Magnitude edge cases: one kind of master and grad values per 128x128 block, so
+# that a small set reaches the ends of the float32 range and the special values.
+# Block kinds (row-major over each param's block grid):
+#   normal      master N(0, 0.02), grad N(0, 1e-3)
+#   tiny        master +-k * 2^-149 (k in 1..100, no zeros), grad 0: the block's
+#               amax / 448 is below half the smallest subnormal
+#   sub_scale   master N(0, 1e-37), grad 0: amax / 448 is a subnormal
+#   huge        master +-[1e38, 3.3e38], grad N(0, 1e-3): amax near FLT_MAX
+#   nan_grad    master N(0, 0.02), grad N(0, 1e-3) with 1 % NaN
+#   inf_grad    master N(0, 0.02), grad N(0, 1e-3) with 1 % +-inf
+#   e8m0_clamp  master +-[2^-131, 1.5 * 2^-125], grad 0: the power-of-two scale
+#               2^(floor(log2 amax) - 8) is below 2^-127 and clamps there
+#   zero        master 0, grad 0
+EDGE_SHAPES = ((1, 256, 512), (1, 200, 300))
+EDGE_KINDS = (
+    (("normal", "tiny", "sub_scale", "huge"), ("nan_grad", "inf_grad", "e8m0_clamp", "zero")),
+    (("normal", "huge", "tiny"), ("nan_grad", "sub_scale", "e8m0_clamp")),
+)
+
+
+def edge_master(pid: int, seed: int = 0) -> np.ndarray:
+    """Row-major [E, R, C] FP32 master of edge param ``pid`` (one kind per block)."""
+    e_n, r, c = EDGE_SHAPES[pid]
+    out = np.zeros((e_n, r, c), np.float32)
+    for br, row in enumerate(EDGE_KINDS[pid]):
+        for bc, kind in enumerate(row):
+            sl = (0, slice(128 * br, min(r, 128 * br + 128)), slice(128 * bc, min(c, 128 * bc + 128)))
+            shape = out[sl].shape
+            rng = _rng(seed, KIND_MASTER, 1000 + pid, br, bc)
+            sign = np.where(rng.random(shape) < 0.5, -1.0, 1.0).astype(np.float32)
+            if kind in ("normal", "nan_grad", "inf_grad"):
+                out[sl] = rng.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
+            elif kind == "tiny":
+                k = rng.integers(1, 101, size=shape).astype(np.uint32)
+                out[sl] = k.view(np.float32) * sign  # k * 2^-149: the subnormal with integer significand k
+            elif kind == "sub_scale":
+                out[sl] = (rng.standard_normal(shape) * 1e-37).astype(np.float32)
+            elif kind == "huge":
+                out[sl] = (rng.uniform(1e38, 3.3e38, size=shape) * sign).astype(np.float32)
+            elif kind == "e8m0_clamp":
+                out[sl] = (rng.uniform(2.0 ** -131, 1.5 * 2.0 ** -125, size=shape) * sign).astype(np.float32)
+    return out
+
+
+def edge_grad(pid: int, step: int, seed: int = 0) -> np.ndarray:
+    """Row-major [E, R, C] FP32 grad of edge param ``pid`` at step ``step``."""
+    e_n, r, c = EDGE_SHAPES[pid]
+    out = np.zeros((e_n, r, c), np.float32)
+    for br, row in enumerate(EDGE_KINDS[pid]):
+        for bc, kind in enumerate(row):
+            sl = (0, slice(128 * br, min(r, 128 * br + 128)), slice(128 * bc, min(c, 128 * bc + 128)))
+            shape = out[sl].shape
+            rng = _rng(seed, KIND_GRAD, 1000 + pid, 1000 * br + bc, step)
+            if kind in ("normal", "huge", "nan_grad", "inf_grad"):
+                g = rng.standard_normal(shape, dtype=np.float32) * np.float32(1e-3)
+                hit = rng.random(shape) < 0.01
+                if kind == "nan_grad":
+                    g[hit] = np.nan
+                elif kind == "inf_grad":
+                    g[hit] = np.where(rng.random(int(hit.sum())) < 0.5, -np.inf, np.inf).astype(np.float32)
+                out[sl] = g
+    return out
+
+
 def get(name: str) -> Workload:
     if name in WORKLOADS:
         return WORKLOADS[name]

@@ -91,3 +91,41 @@ def unfold_all_ranks(w, tabs, per_rank_arrays: Dict[int, np.ndarray], dtype, sca
     for r, arr in per_rank_arrays.items():
         layout.unfold_shard(tabs[r], arr, dst, None if scales is None else scales[r], dsc)
     return dst, dsc
+
+
+# ---------------------------------------------------------------- two-stage clip check
+#
+# The float64 sum of squares is the one result of the step whose value depends on a
+# reduction order: the GPU and the oracle sum in different orders, agree to ~1e-16
+# relative, and the clip-and-unscale factor k (rounded to float32) is then almost
+# always equal.  Stage 1 checks the sums within 1e-12 and that the GPU's k is the
+# oracle's finalize applied to the GPU's own sum; stage 2 re-runs the oracle's step
+# with the GPU's k when the two k differ, and everything else must then be bit-exact.
+
+def initial_reference(w, tab) -> dict:
+    """The oracle's folded buffers and state before step 1 (the init fold of the masters)."""
+    n = tab["shard_slots"]
+    z = np.zeros((n, 128, 128), np.float32)
+    return dict(state=optim.init_state(w.hp), master=layout.fold_shard(tab, masters(w)), m=z, v=z.copy(),
+                codes=np.zeros((n, 128, 128), np.uint8), scales=np.zeros(n, np.float32))
+
+
+def clip_stage1(hp, prev_state: dict, got: dict, want: dict, tag: str = ""):
+    """Returns None when the GPU's k equals the oracle's, else the GPU's k after checking
+    that it follows from the GPU's sum of squares (within 1e-12 of the oracle's)."""
+    a, b = got["global_sumsq"], want["global_sumsq"]
+    if not (np.isinf(a) and np.isinf(b)) and not (np.isnan(a) and np.isnan(b)):
+        assert abs(a - b) <= 1e-12 * abs(b), (tag, "global_sumsq", a, b)
+    if got["k"] == want["k"]:
+        return None
+    assert got["found_inf"] == want["found_inf"] == 0, (tag, "k differs on a skipped step")
+    k = optim.finalize(prev_state, hp, a, 0.0)["k"]
+    assert got["k"] == k, (tag, "GPU k is not the finalize of its own sum", got["k"], k)
+    return got["k"]
+
+
+def step_given_k(w, tab, prev: dict, grad, extra: float, k: float) -> dict:
+    """Stage 2: the oracle's step from the reference buffers ``prev`` with factor k."""
+    st, mas, m, v, c, sc = step.step_sharded(tab, w.hp, prev["state"], grad, prev["master"], prev["m"], prev["v"],
+                                             prev["codes"], prev["scales"], extra_sumsq=extra, k=k)
+    return dict(state=st, master=mas, m=m, v=v, codes=c, scales=sc, grad=grad, extra=extra)

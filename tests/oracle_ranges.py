@@ -83,8 +83,10 @@ STATE_KEYS = ("step", "found_inf", "skipped_total", "good_steps", "k", "loss_sca
 
 def range_run(job) -> dict:
     """Init fold of the weights, then ``steps`` oracle steps on the range; returns the
-    state after every step and digests of the final folded master, m, v, codes, scales."""
-    name, rank, split, s0, s1, steps, extras = job
+    state after every step and digests of the final folded master, m, v, codes, scales.
+    ``ks`` (or None): per step, a clip-and-unscale factor to use instead of the
+    finalize's (the second stage of the clip check), or None for the finalize's own."""
+    name, rank, split, s0, s1, steps, extras, ks = job
     w, sub = sub_table(name, rank, split, s0, s1)
     if w.master_dtype == "bf16":
         master = _fold(sub, lambda p, e: layout.widen_bf16(synth.master_slab_bf16(w, p, e)))
@@ -101,7 +103,7 @@ def range_run(job) -> dict:
         g = _fold(sub, lambda p, e: synth.grad_slab(w, p, e, t))
         extra = 0.0 if extras is None else extras[t - 1]
         st, master, m, v, codes, scales = ostep.step_sharded(sub, w.hp, st, g, master, m, v, codes, scales,
-                                                             extra_sumsq=extra)
+                                                             extra_sumsq=extra, k=None if ks is None else ks[t - 1])
         del g
         states.append({k: st[k] for k in STATE_KEYS})
     return {"states": states, "master": digest(master), "m": digest(m), "v": digest(v), "codes": digest(codes),

@@ -11,6 +11,7 @@ import pytest
 
 import synth
 from oracle import layout, optim, step as ostep, table as otable
+from tests import harness
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -140,16 +141,21 @@ def test_full_size_sampled(name, steps, fold_on_read):
         del G
         sh.step(hp, grads, dst_codes, dst_scales, fused_stats=True, fold_on_read=fold_on_read)
         del grads
-        st, master, m, v, codes, sc = ostep.step_sharded(sub, w.hp, st, g_sub, master, m, v, codes, sc,
-                                                         extra_sumsq=extra)
         torch.cuda.synchronize()
         gst = sh.read_state()
         tag = f"{name} step {t}"
+        prev = (st, master, m, v, codes, sc)
+        st, master, m, v, codes, sc = ostep.step_sharded(sub, w.hp, st, g_sub, master, m, v, codes, sc,
+                                                         extra_sumsq=extra)
+        if stats:
+            # two-stage clip check: sums within 1e-12; a k that differs by the sum order is
+            # checked to follow from the GPU's sum, and the oracle's step re-run with it
+            k_gpu = harness.clip_stage1(w.hp, prev[0], gst, st, tag)
+            if k_gpu is not None:
+                st, master, m, v, codes, sc = ostep.step_sharded(sub, w.hp, *prev[:1], g_sub, *prev[1:],
+                                                                 extra_sumsq=extra, k=k_gpu)
         for key in ("step", "found_inf", "k", "loss_scale", "step_size", "bc2_sqrt", "decay"):
             assert gst[key] == st[key], (tag, key, gst[key], st[key])
-        if stats:
-            assert abs(gst["global_sumsq"] - st["global_sumsq"]) <= 1e-12 * abs(st["global_sumsq"]) or \
-                (np.isinf(gst["global_sumsq"]) and np.isinf(st["global_sumsq"]))
 
         def rows(x, dt=torch.float32):
             return x.view(-1, BLOCK)[idx].cpu().numpy().reshape(n, 128, 128)

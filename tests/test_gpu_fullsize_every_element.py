@@ -18,8 +18,8 @@ import numpy as np
 import pytest
 
 import synth
-from oracle import layout, table as otable
-from tests import oracle_ranges as orr
+from oracle import layout, optim, table as otable
+from tests import harness, oracle_ranges as orr
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -54,13 +54,16 @@ def _range_digests(host: np.ndarray, rr, unit: int):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,steps", [("moe", 3), ("full", 5), ("ragged", 3), ("dense", 10)])
-def test_every_element_full_size(name, steps):
+@pytest.mark.parametrize("name,steps,split", [("moe", 5, None), ("full", 5, None), ("ragged", 3, None),
+                                              ("ragged", 3, "param"), ("dense", 10, None)])
+def test_every_element_full_size(name, steps, split):
     fz = _fz()
     from blockwise_fp8_zero_fold_amd.shard import Shard
     from tests import gpu_harness as gh
 
     w = synth.get(name)
+    if split:
+        w = w.with_(split=split)
     rank = w.ranks[0]
     tab = otable.build(w.shapes, w.dp, rank, otable.PARAM if w.split == "param" else otable.BLOCK)
     ent = tab["entries"]
@@ -102,8 +105,26 @@ def test_every_element_full_size(name, steps):
             del grads
             print(f"[{name}] GPU step {t} done", flush=True)
 
-        extras = orr.extras_for(sums.get(timeout=600), other) if stats else [None] * len(rr)
-        run = pool.map_async(orr.range_run, [(name, rank, w.split, a, b, steps, extras[i])
+        ks = None
+        if stats:
+            mine = sums.get(timeout=600)
+            extras = orr.extras_for(mine, other)
+            # two-stage clip check: the sums within 1e-12, and where the GPU's k differs
+            # from the oracle's (another summation order) the oracle runs with the GPU's k
+            tot = [sum(s[t] for s in mine) + (other[t] if other else 0.0) for t in range(steps)]
+            st = optim.init_state(w.hp)
+            ks = []
+            for t in range(steps):
+                want_st = optim.finalize(st, w.hp, tot[t], 0.0)
+                assert gpu_states[True][t]["k"] == gpu_states[False][t]["k"], (name, "routes' k differ", t + 1)
+                k = harness.clip_stage1(w.hp, st, gpu_states[True][t], want_st, f"{name} step {t + 1}")
+                ks.append(k)
+                st = want_st if k is None else dict(want_st, k=k)
+            if all(k is None for k in ks):
+                ks = None
+        else:
+            extras = [None] * len(rr)
+        run = pool.map_async(orr.range_run, [(name, rank, w.split, a, b, steps, extras[i], ks)
                                              for i, (a, b) in enumerate(rr)])
 
         # the GPU's results, hashed by the same slot ranges, while the oracle runs

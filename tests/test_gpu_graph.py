@@ -75,6 +75,8 @@ def test_captured_step_replays_equal_oracle(fold_on_read, fused):
     torch.cuda.synchronize()
     _check(gh, sh, tab, ref[0][0], un[0], held, codes, scales, f"{tag} step 1 (eager)")
 
+    heldmask = {p: np.zeros(s, bool) for p, s in enumerate(w.shapes)}
+    layout.unfold_shard(tab, layout.valid_mask(tab), heldmask)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         run()
@@ -91,6 +93,19 @@ def test_captured_step_replays_equal_oracle(fold_on_read, fused):
         g.replay()
         torch.cuda.synchronize()
         _check(gh, sh, tab, ref[0][t - 1], un[t - 1], held, codes, scales, f"{tag} step {t} (replay)")
+        if t > 2:  # the FP32 read-back of the previous replay must not have been written over
+            for p in held:
+                assert gh.bits_equal(readback[p].cpu().numpy()[heldmask[p]], want_rb[p][heldmask[p]]), (tag, t, p)
+        # an uncaptured FP32 unfold of the master into new arrays between replays: it has
+        # its own pointer list, so the next replay still writes codes where it was captured to
+        readback = [torch.zeros(s, dtype=torch.float32, device="cuda") if p in held else None
+                    for p, s in enumerate(w.shapes)]
+        fz.fp8z1_unfold(sh.table, sh.master, fz.F32, None, readback)
+        torch.cuda.synchronize()
+        want_rb = {p: np.zeros(s, np.float32) for p, s in enumerate(w.shapes)}
+        layout.unfold_shard(tab, ref[0][t - 1]["master"], want_rb)
+        for p in held:
+            assert gh.bits_equal(readback[p].cpu().numpy()[heldmask[p]], want_rb[p][heldmask[p]]), (tag, t, p)
     assert any(r["state"]["found_inf"] for r in ref[0][1:]), "a skipped step must be among the replays"
     del g
 

@@ -251,6 +251,8 @@ def _run_parity(w, ranks=None, fused=None, fold_on_read=False):
         for e in tab["entries"]:
             if e["param"] >= 0:
                 blockmask[int(e["param"])][int(e["expert"]), int(e["brow"]), int(e["bcol"])] = True
+        prev = harness.initial_reference(w, tab)
+        rederived = False  # the reference chain left the precomputed one (a k that differed)
         for t in range(1, w.steps + 1):
             R = ref[r][t - 1]
             hp = fz.Hparams.make(w.hp, extra_sumsq=R["extra"])
@@ -261,14 +263,19 @@ def _run_parity(w, ranks=None, fused=None, fold_on_read=False):
             if not fold_on_read:
                 assert gh.bits_equal(gh.folded(sh.grad, n), R["grad"]), f"{tag}: grad fold"
             st = sh.read_state()
+            if rederived:
+                R = harness.step_given_k(w, tab, prev, R["grad"], R["extra"], None)
+            k_gpu = harness.clip_stage1(w.hp, prev["state"], st, R["state"], tag)
+            if k_gpu is not None:  # stage 2: the oracle's step with the GPU's k
+                print(f"# {tag}: k differs from the oracle's by the sum order; stage 2 with k={k_gpu!r}")
+                R = harness.step_given_k(w, tab, prev, R["grad"], R["extra"], k_gpu)
+                rederived = True
+            prev = R
             want_st = R["state"]
             for key in ("step", "found_inf", "skipped_total", "good_steps"):
                 assert st[key] == want_st[key], (tag, key, st[key], want_st[key])
             for key in ("k", "loss_scale", "step_size", "bc2_sqrt", "decay", "beta1_pow", "beta2_pow"):
                 assert st[key] == want_st[key], (tag, key, st[key], want_st[key])
-            if want_st["global_sumsq"] != 0 or st["global_sumsq"] != 0:
-                a, b = st["global_sumsq"], want_st["global_sumsq"]
-                assert (np.isinf(a) and np.isinf(b)) or abs(a - b) <= 1e-12 * abs(b), (tag, a, b)
             for name, dt in (("master", np.float32), ("m", np.float32), ("v", np.float32)):
                 got = gh.folded(getattr(sh, name), n)
                 _bar(got[mask], R[name][mask], f"{tag}: {name}")
@@ -280,6 +287,10 @@ def _run_parity(w, ranks=None, fused=None, fold_on_read=False):
             _bar(got_sc, R["scales"], f"{tag}: scales")
             assert gh.bits_equal(got_sc, R["scales"]), f"{tag}: scales not bit-exact"
             U = un[t - 1]
+            if rederived and R["state"]["step"] > 0:
+                # the unsharded run used the oracle's own k: unfold the re-derived shard instead
+                U = dict(zip(("codes", "scales"), harness.unfold_all_ranks(w, {r: tab}, {r: R["codes"]}, np.uint8,
+                                                                          scales={r: R["scales"]})))
             if U["codes"] is not None:
                 for p in held:
                     c = codes[p].cpu().numpy()

@@ -27,7 +27,7 @@ def test_ranges_equal_whole_shard(name, parts):
             whole = [orr.slab_sumsq((name, p, e, w.steps)) for p, (E, _, _) in enumerate(w.shapes) for e in range(E)]
             other = [sum(s[t] for s in whole) - sum(s[t] for s in sums) for t in range(w.steps)]
         extras = orr.extras_for(sums, other)
-    res = [orr.range_run((name, rank, w.split, a, b, w.steps, extras[i])) for i, (a, b) in enumerate(rr)]
+    res = [orr.range_run((name, rank, w.split, a, b, w.steps, extras[i], None)) for i, (a, b) in enumerate(rr)]
     last = ref[rank][w.steps - 1]
     for t in range(w.steps):
         for key, val in res[0]["states"][t].items():

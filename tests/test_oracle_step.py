@@ -104,3 +104,64 @@ def test_padding_slots_get_unit_scale_and_zero_codes():
                             np.zeros(n, np.float32))
     pad = ent["param"] < 0
     assert (out[5][pad] == 1.0).all() and (out[4][pad] == 0).all()
+
+
+def test_k_override_enters_where_the_grad_is_scaled():
+    """The second stage of the clip check re-runs the step with a given clip-and-unscale
+    factor k.  Scaling by a power of two is exact, so the step with factor 2k on grads g
+    must equal the step with factor k on grads 2g bit for bit (no overflow or subnormal
+    grads here); and the factor the finalize derives, given back as k, changes nothing."""
+    w = synth.get("tiny_clip")
+    tab = table.build(w.shapes, w.dp, 1, table.BLOCK)
+    n = tab["shard_slots"]
+    P = layout.fold_shard(tab, harness.masters(w))
+    g = layout.fold_shard(tab, harness.grads(w, 1))
+    z = np.zeros((n, 128, 128), np.float32)
+    codes, sc = np.zeros((n, 128, 128), np.uint8), np.zeros(n, np.float32)
+    st0 = optim.init_state(w.hp)
+    base = step.step_sharded(tab, w.hp, st0, g, P, z, z, codes, sc, extra_sumsq=3.0)
+    k = base[0]["k"]
+    assert 0 < k < 1
+    same = step.step_sharded(tab, w.hp, st0, g, P, z, z, codes, sc, extra_sumsq=3.0, k=k)
+    for a, b in zip(base[1:], same[1:]):
+        assert a.tobytes() == b.tobytes()
+    k2 = float(np.float32(2 * k))
+    x = step.step_sharded(tab, w.hp, st0, g, P, z, z, codes, sc, extra_sumsq=3.0, k=k2)
+    y = step.step_sharded(tab, w.hp, st0, (2 * g).astype(np.float32), P, z, z, codes, sc, extra_sumsq=3.0, k=k)
+    assert x[0]["k"] == k2 and y[0]["k"] == k
+    for a, b in zip(x[1:], y[1:]):
+        assert a.tobytes() == b.tobytes()
+    assert x[1].tobytes() != base[1].tobytes()  # the factor is used
+
+
+def test_two_stage_clip_check_accepts_a_sum_order_flip_only():
+    """The harness's stage 1 on a global sum placed where the float32 rounding of k
+    flips: a GPU sum 1e-13 away (another summation order) with the k its own finalize
+    gives is accepted and returned for stage 2; a k that does not follow from the GPU's
+    sum, or a sum outside 1e-12, is rejected."""
+    w = synth.get("tiny_clip")
+    hp = w.hp
+    st0 = optim.init_state(hp)
+    # c = max_norm / (sqrt(G) + 1e-6) lands on the midpoint of two float32 values
+    lo = np.float32(0.3)
+    hi = np.nextafter(lo, np.float32(1))
+    mid = (float(lo) + float(hi)) / 2
+    G = (float(np.float32(hp.max_grad_norm)) / mid - 1e-6) ** 2
+    ks = {}
+    for d in (-1e-13, 1e-13):
+        ks[d] = optim.finalize(st0, hp, G * (1 + d), 0.0)["k"]
+    assert ks[-1e-13] != ks[1e-13], "the test sum must sit on a rounding boundary"
+    want = optim.finalize(st0, hp, G * (1 - 1e-13), 0.0)
+    got = dict(want, global_sumsq=G * (1 + 1e-13), k=ks[1e-13])
+    assert harness.clip_stage1(hp, st0, got, want) == ks[1e-13]
+    assert harness.clip_stage1(hp, st0, dict(want), want) is None
+    with pytest.raises(AssertionError):  # k not derived from the GPU's own sum
+        harness.clip_stage1(hp, st0, dict(want, global_sumsq=G * (1 - 1e-13), k=ks[1e-13]), want)
+    with pytest.raises(AssertionError):  # sums too far apart
+        harness.clip_stage1(hp, st0, dict(want, global_sumsq=G * (1 + 1e-11)), want)
+    # stage 2 with the flipped k equals the oracle step given that k
+    tab = table.build(w.shapes, w.dp, 1, table.BLOCK)
+    prev = harness.initial_reference(w, tab)
+    g = layout.fold_shard(tab, harness.grads(w, 1))
+    R = harness.step_given_k(w, tab, prev, g, 0.0, ks[1e-13])
+    assert R["state"]["k"] == ks[1e-13]

@@ -129,3 +129,43 @@ def test_small_variants_keep_their_structure(name):
     w = synth.get(name)
     assert w.steps >= 2 and len(w.ranks) >= 1 and all(0 <= r < w.dp for r in w.ranks)
     assert w.total_elems() < 50_000_000  # the oracle finishes these in seconds
+
+
+def test_edge_inputs_reach_their_cases():
+    """The magnitude edge inputs (one kind per block) reach what each kind is for, in the
+    oracle: a scale that rounds to 0, a subnormal scale, an amax near FLT_MAX, the
+    power-of-two scale clamped at 2^-127, NaN and inf grads, an all-zero block."""
+    import numpy as np
+    from oracle import layout, optim, step as ostep, table as otable
+
+    kinds = [k for rows in synth.EDGE_KINDS for row in rows for k in row]
+    tab = otable.build(synth.EDGE_SHAPES, 1, 0, otable.BLOCK)
+    assert len(kinds) == tab["shard_slots"]
+    P = {p: synth.edge_master(p) for p in range(len(synth.EDGE_SHAPES))}
+    G = {p: synth.edge_grad(p, 1) for p in range(len(synth.EDGE_SHAPES))}
+    gf = layout.fold_shard(tab, G)
+    mask = layout.valid_mask(tab)
+    for rule in (0, 1):
+        hp = synth.Hparams(scale_rule=rule)
+        n = tab["shard_slots"]
+        z = np.zeros((n, 128, 128), np.float32)
+        st, master, m, v, codes, sc = ostep.step_sharded(tab, hp, optim.init_state(hp), gf,
+                                                         layout.fold_shard(tab, P), z, z,
+                                                         np.zeros((n, 128, 128), np.uint8), np.zeros(n, np.float32))
+        for i, k in enumerate(kinds):
+            real = mask[i]
+            if k == "tiny":
+                assert sc[i] == (0.0 if rule == 0 else 2.0 ** -127)
+                assert (master[i][real] != 0).all()  # no exact zeros (0/0 would be a NaN code)
+            if k == "sub_scale" and rule == 0:
+                assert 0 < sc[i] < np.finfo(np.float32).tiny
+            if k == "huge":
+                assert np.abs(master[i][real]).max() > 3e38 and np.isfinite(master[i][real]).all()
+            if k == "e8m0_clamp" and rule == 1:
+                assert sc[i] == 2.0 ** -127
+            if k == "nan_grad":
+                assert np.isnan(gf[i][real]).any() and np.isnan(master[i][real]).any()
+            if k == "inf_grad":
+                assert np.isinf(gf[i][real]).any() and np.isnan(master[i][real]).any()
+            if k == "zero":
+                assert sc[i] == 1.0 and (codes[i] == 0).all()
