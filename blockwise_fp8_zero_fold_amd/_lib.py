@@ -20,6 +20,7 @@ F32, BF16, E4M3 = 0, 1, 2
 SCALE_AMAX, SCALE_POW2 = 0, 1
 SPLIT_BLOCK, SPLIT_PARAM = 0, 1
 STAT_PARTS = 4  # float64 partial sums of squares per slot
+NOALLOC_MAX_SLOTS = 262144  # largest table fp8z1_step_rowmajor_noalloc takes
 ALL_RANKS = -1
 
 BLOCK_ENTRY_DTYPE = np.dtype([
@@ -100,6 +101,8 @@ _sig = {
                              _vp]),
     "fp8z1_step_rowmajor": (C.c_int, [_vp, C.POINTER(Hparams), _vp, C.POINTER(_vp), _vp, _vp, _vp, _vp, _vp, _vp,
                                       C.c_size_t, _vp]),
+    "fp8z1_step_rowmajor_noalloc": (C.c_int, [_vp, C.POINTER(Hparams), _vp, C.POINTER(_vp), _vp, _vp, _vp, _vp,
+                                              _vp, _vp]),
     "fp8z1_unfold": (C.c_int, [_vp, _vp, C.c_int32, _vp, C.POINTER(_vp), C.POINTER(_vp), _vp]),
     "fp8z1_state_read": (C.c_int, [_vp, C.POINTER(State), _vp]),
     "fp8z1_state_write": (C.c_int, [_vp, C.POINTER(State), _vp]),
@@ -302,6 +305,22 @@ def fp8z1_step_rowmajor(table: Table, hp: Hparams, d_state, grads: Sequence, mas
     _check(lib.fp8z1_step_rowmajor(table.handle, C.byref(hp), _ptr(d_state), _ptr_list(grads), _ptr(master), _ptr(m),
                                    _ptr(v), _ptr(fp8), _ptr(scales), _ptr(workspace), workspace_bytes,
                                    _stream(stream)), "fp8z1_step_rowmajor")
+
+
+def fp8z1_step_rowmajor_noalloc(table: Table, hp: Hparams, d_state, grads: Sequence, master, m, v, fp8, scales,
+                                stream=None) -> None:
+    """fp8z1_step_rowmajor without a workspace: the library keeps the statistics partials
+    in its own device array, so the call allocates nothing."""
+    n = table.shard_slots
+    for name, x in (("master", master), ("m", m), ("v", v)):
+        _need(x, n * 16384 * 4, f"step_rowmajor_noalloc {name}")
+    _need(fp8, n * 16384, "step_rowmajor_noalloc fp8")
+    _need(scales, n * 4, "step_rowmajor_noalloc scales")
+    _need(d_state, 64, "step_rowmajor_noalloc state")
+    _check_param_list(table, grads, F32, "step_rowmajor_noalloc grads")
+    _check(lib.fp8z1_step_rowmajor_noalloc(table.handle, C.byref(hp), _ptr(d_state), _ptr_list(grads), _ptr(master),
+                                           _ptr(m), _ptr(v), _ptr(fp8), _ptr(scales), _stream(stream)),
+           "fp8z1_step_rowmajor_noalloc")
 
 
 def fp8z1_unfold(table: Table, folded, dtype: int, scales, dsts: Sequence, dst_scales: Optional[Sequence] = None,

@@ -696,6 +696,63 @@ extern "C" int fp8z1_step_rowmajor(const fp8z1_table* ct, const fp8z1_hparams* h
                    d_workspace, workspace_bytes, 0, stream);
 }
 
+// ---------------------------------------------------------------- no allocation
+//
+// The statistics partials of fp8z1_step_rowmajor_noalloc: a file-scope device
+// array, one copy per GPU.  In host code `scratch` names a host-side stand-in,
+// not device memory; its device address on each GPU comes from
+// hipGetSymbolAddress, taken once per device (with that device current) at the
+// first call there, and only that address is passed to kernels.
+namespace {
+constexpr int64_t kNoallocSlots = FP8Z1_NOALLOC_MAX_SLOTS;
+static __device__ __align__(256) double scratch[kNoallocSlots * kStatParts];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+double* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_device(double** out) {
+  int dev = -1;
+  int rc = check_hip(hipGetDevice(&dev), "step_rowmajor_noalloc: hipGetDevice");
+  if (rc) return rc;
+  if (dev < 0 || dev >= kMaxDevices)
+    return set_error(FP8Z1_EDEVICE, "step_rowmajor_noalloc: device index " + std::to_string(dev) + " beyond " +
+                                         std::to_string(kMaxDevices));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    rc = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "step_rowmajor_noalloc: hipGetSymbolAddress");
+    if (rc) return rc;
+    g_scratch_ptr[dev] = static_cast<double*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return FP8Z1_OK;
+}
+}  // namespace
+
+extern "C" int fp8z1_step_rowmajor_noalloc(const fp8z1_table* ct, const fp8z1_hparams* hp, fp8z1_state* d_state,
+                                           const void* const* grads, float* master, float* m, float* v, uint8_t* fp8,
+                                           float* scales, void* stream) {
+  fp8z1_table* t = const_cast<fp8z1_table*>(ct);
+  if (!t || !hp || !grads) return set_error(FP8Z1_EINVAL, "step_rowmajor_noalloc: NULL argument");
+  if (t->info.shard_slots > kNoallocSlots)
+    return set_error(FP8Z1_ESHAPE, "step_rowmajor_noalloc: the table has " + std::to_string(t->info.shard_slots) +
+                                       " slots, more than FP8Z1_NOALLOC_MAX_SLOTS (" + std::to_string(kNoallocSlots) +
+                                       "); use fp8z1_step_rowmajor with a workspace");
+  {
+    std::lock_guard<std::mutex> lock(t->mu);
+    if (t->device < 0)
+      return set_error(FP8Z1_EINVAL,
+                       "step_rowmajor_noalloc: the table is not set up on a device yet (setting it up allocates); "
+                       "make one other GPU call with it first, e.g. the init fp8z1_fold");
+  }
+  double* ws = nullptr;
+  const int rc = scratch_on_device(&ws);
+  if (rc) return rc;
+  return step_impl(t, hp, d_state, nullptr, grads, master, m, v, fp8, scales, ws,
+                   static_cast<size_t>(kNoallocSlots) * kStatParts * sizeof(double), 0, stream);
+}
+
 extern "C" int fp8z1_encode_e4m3(const float* in, uint8_t* out, int64_t n, void* stream) {
   if (n < 0 || (n > 0 && (!in || !out))) return set_error(FP8Z1_EINVAL, "encode_e4m3: bad arguments");
   if (n == 0) return FP8Z1_OK;

@@ -262,6 +262,26 @@ int fp8z1_step_rowmajor(const fp8z1_table* table, const fp8z1_hparams* hp, fp8z1
                         const void* const* grads, float* master, float* m, float* v, uint8_t* fp8, float* scales,
                         void* d_workspace, size_t workspace_bytes, void* stream);
 
+/* fp8z1_step_rowmajor for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The call allocates nothing: the statistics partials live in a
+ * device array of the library (FP8Z1_NOALLOC_MAX_SLOTS * FP8Z1_STAT_PARTS
+ * float64 = 8 MiB on each GPU that runs the call, held until the process
+ * ends) instead of a caller workspace.  Same arguments, results and errors as
+ * fp8z1_step_rowmajor, and bit-identical results, with these limits:
+ *   - tables of more than FP8Z1_NOALLOC_MAX_SLOTS slots: FP8Z1_ESHAPE;
+ *   - the table must already be set up on the current device (any earlier
+ *     GPU call with it, e.g. the init fp8z1_fold of the masters), because
+ *     setting it up allocates: else FP8Z1_EINVAL;
+ *   - every call on one GPU uses that GPU's one array, which keeps the last
+ *     call's partials (each call writes all the partials it reads before it
+ *     reads them): calls that may overlap on one GPU (other streams, other
+ *     threads, not ordered by the caller) race on it. */
+#define FP8Z1_NOALLOC_MAX_SLOTS 262144
+int fp8z1_step_rowmajor_noalloc(const fp8z1_table* table, const fp8z1_hparams* hp, fp8z1_state* d_state,
+                                const void* const* grads, float* master, float* m, float* v, uint8_t* fp8,
+                                float* scales, void* stream);
+
 /* Unfold (section "参数布局变换", and the scale unfold of section "总结"):
  * write the shard's real elements from `folded` (device, shard_slots*16384
  * elements of dtype FP8Z1_E4M3 or FP8Z1_F32) into row-major params.

@@ -155,7 +155,8 @@ def test_workspace_bytes_and_constants_match_header():
     defs = dict(re.findall(r"#define (FP8Z1_[A-Z0-9_]+) \(?(-?\d+)\)?", text))
     for name, val in (("F32", fz.F32), ("BF16", fz.BF16), ("E4M3", fz.E4M3), ("SCALE_AMAX", fz.SCALE_AMAX),
                       ("SCALE_POW2", fz.SCALE_POW2), ("SPLIT_BLOCK", fz.SPLIT_BLOCK), ("SPLIT_PARAM", fz.SPLIT_PARAM),
-                      ("ALL_RANKS", fz.ALL_RANKS), ("STAT_PARTS", fz.STAT_PARTS)):
+                      ("ALL_RANKS", fz.ALL_RANKS), ("STAT_PARTS", fz.STAT_PARTS),
+                      ("NOALLOC_MAX_SLOTS", fz.NOALLOC_MAX_SLOTS)):
         assert int(defs["FP8Z1_" + name]) == val, name
     for name in ("tiny", "ragged_small"):
         w = synth.get(name)
