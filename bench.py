@@ -122,11 +122,12 @@ def _source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic(workload: str, mode: str, src_hash: str):
+def _traffic(workload: str, mode: str, src_hash: str, split: str = ""):
     """HBM bytes (read + written) per launch of the dominant kernel from the committed
-    rocprofv3 counter summary, or None when the kernels changed since the counters
-    were taken."""
-    path = os.path.join(ROOT, "profiles", f"update_kernel_{workload}_{mode}_pmc.json")
+    rocprofv3 counter summary of this workload (and split, when it is not the
+    workload's own), or None when there is none or the kernels changed since the
+    counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"update_kernel_{workload}{split}_{mode}_pmc.json")
     if not os.path.exists(path):
         return None
     try:
@@ -722,7 +723,8 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": _traffic(w.name, args.mode, src_hash),
+            "traffic": _traffic(w.name, args.mode, src_hash,
+                                "" if w.split == synth.get(w.name).split else f"_{w.split}"),
             "bytes_per_launch": call_bytes,
         },
         "ceiling": ceiling,

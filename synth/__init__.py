@@ -192,6 +192,11 @@ SMALL_WORKLOADS = {
     "ragged_small_pow2": Workload(
         name="ragged_small_pow2", shapes=ragged_shapes(1, 40, 64, 700, (1, 3)), dp=16,
         ranks=(0, 7, 15), steps=2, hp=dataclasses.replace(TINY_HP, scale_rule=1), grad_sigma=1e-3),
+    # long ragged rows (40,000 columns: one unfold work item per row of a block row)
+    # next to short ones
+    "wide_rows_small": Workload(
+        name="wide_rows_small", shapes=((1, 150, 40000), (1, 300, 520)), dp=2, ranks=(0, 1), steps=2,
+        hp=TINY_HP, grad_sigma=1e-3),
     "full_small": Workload(
         name="full_small", shapes=((4, 300, 520),), dp=1, ranks=(0,), steps=5,
         hp=dataclasses.replace(TINY_HP, max_grad_norm=1.0, loss_scaling=True, init_scale=65536.0),

@@ -117,13 +117,14 @@ def test_fold_unfold_bit_exact(name, split):
         t.free()
 
 
-@pytest.mark.parametrize("name", ["moe_small", "ragged_small", "full_small"])
+@pytest.mark.parametrize("name", ["moe_small", "ragged_small", "full_small", "wide_rows_small"])
 def test_unfold_codes_at_any_destination_alignment(name):
     """FP8 unfold of random codes (padding bytes random too: they must be dropped) into
     destinations at byte offsets 0, 1, 16, 64 and 127 of a sentinel-filled buffer: the
     shard's real positions get the oracle's bytes, no other byte (inside the param or in
     the margins around it) changes; scales land in [E, Rb, Cb].  Covers both unfold
-    kernels (by blocks when rows start on 128-byte lines, by rows otherwise)."""
+    kernels (by blocks when rows start on 128-byte lines, by rows otherwise), with
+    rows up to 40,000 codes long."""
     gh = _gh()
     w = synth.get(name)
     rng = np.random.default_rng(17)
