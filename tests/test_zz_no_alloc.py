@@ -96,3 +96,54 @@ def test_noalloc_refusals():
     assert "FP8Z1_NOALLOC_MAX_SLOTS" in _lib.lib.fp8z1_last_error().decode()
     big.free()
     t.free()
+
+
+def test_noalloc_step_captured_in_a_graph():
+    """The callers the entry point is for: the no-alloc step captured once into a HIP
+    graph (full_small: clipping, loss scaling, an inf grad that skips step 3) and
+    replayed step after step with new grads copied into the captured buffers; after
+    every replay the state and folded buffers equal those of an eager twin shard stepped
+    by fp8z1_step_rowmajor with a workspace, bit for bit."""
+    fz = _fz()
+    from blockwise_fp8_zero_fold_amd.shard import Shard
+    from tests import gpu_harness as gh
+
+    w = synth.get("full_small")
+    tab = otable.build(w.shapes, w.dp, 0, otable.BLOCK)
+    held = gh.held_experts(tab["entries"])
+    masters = gh.master_tensors(w, held)
+    a, b = Shard(w.shapes, w.dp, 0), Shard(w.shapes, w.dp, 0)
+    for sh in (a, b):
+        sh.init(fz.Hparams.make(w.hp), masters, fz.BF16)
+    n = a.n_slots
+    hp = fz.Hparams.make(w.hp)
+    grads = gh.grad_tensors(w, held, 1)  # the captured grad buffers
+
+    def noalloc():
+        fz.fp8z1_step_rowmajor_noalloc(b.table, hp, b.state, grads, b.master, b.m, b.v, b.fp8, b.scales)
+
+    noalloc()  # eager step 1 (uploads this grad pointer list)
+    a.update_rowmajor(hp, grads)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        noalloc()
+    torch.cuda.synchronize()
+    for t in range(2, w.steps + 1):
+        new = gh.grad_tensors(w, held, t)
+        for dst, src in zip(grads, new):
+            if dst is not None:
+                dst.copy_(src)
+        torch.cuda.synchronize()
+        g.replay()
+        a.update_rowmajor(hp, grads)
+        torch.cuda.synchronize()
+        tag = f"graph replay for step {t}"
+        sa, sb = a.read_state(), b.read_state()
+        assert sa == sb, (tag, sa, sb)
+        for name in ("master", "m", "v"):
+            assert gh.bits_equal(gh.folded(getattr(a, name), n), gh.folded(getattr(b, name), n)), f"{tag}: {name}"
+        assert gh.bits_equal(gh.folded(a.fp8, n, np.uint8), gh.folded(b.fp8, n, np.uint8)), f"{tag}: codes"
+        assert gh.bits_equal(a.scales.cpu().numpy()[:n], b.scales.cpu().numpy()[:n]), f"{tag}: scales"
+    assert sb["skipped_total"] == 1 and 0 < sb["k"] < 1
+    del g
