@@ -639,6 +639,7 @@ def main() -> int:
     total_bytes, call_bytes = step_bytes(args.mode)
     achieved = call_bytes / (ms["step"] * 1e-3) / 1e9
     src_hash = _source_hash()
+    traffic_split = "" if w.split == synth.get(w.name).split else f"_{w.split}"
     alt_mode = modes[1]
     alt_ms, alt_calls = results[alt_mode]
     alt_total, _ = step_bytes(alt_mode)
@@ -723,8 +724,11 @@ def main() -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": _traffic(w.name, args.mode, src_hash,
-                                "" if w.split == synth.get(w.name).split else f"_{w.split}"),
+            "traffic": _traffic(w.name, args.mode, src_hash, traffic_split),
+            # where `traffic` comes from: the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of
+            # this workload and route, used only while the kernel sources hash to its recorded value
+            "traffic_source": (f"profiles/update_kernel_{w.name}{traffic_split}_{args.mode}_pmc.json"
+                               f" (kernel sources {src_hash})"),
             "bytes_per_launch": call_bytes,
         },
         "ceiling": ceiling,

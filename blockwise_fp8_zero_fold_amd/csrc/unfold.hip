@@ -21,6 +21,7 @@ namespace fp8z1 {
 namespace {
 
 constexpr int kUnfThreads = 256;
+constexpr int kUnfBatch = 4;
 
 // Bytes [sh, sh + 16) of the 32 bytes lo || hi (lo first), sh in [0, 16).
 __device__ __forceinline__ uint4 funnel16(const uint4 lo, const uint4 hi, int sh) {
@@ -48,7 +49,11 @@ __device__ __forceinline__ uint4 funnel16(const uint4 lo, const uint4 hi, int sh
 // shuffle; the first lane of a wave and the first chunk of a row load it).
 // Chunks wholly inside the row are one aligned (streaming) store; the first
 // and last chunk of a row are written byte by byte, only the row's own bytes,
-// so no byte outside the run is ever written.
+// so no byte outside the run is ever written.  A lane takes kUnfBatch chunks
+// per round and issues all their loads before any shuffle or store (an item
+// of ~16 KB is one round): on the ragged shard 294 us against 325 us with one
+// chunk per round, where a lane that needed chunk k - 1 itself loaded it only
+// after the shuffle.
 __global__ __launch_bounds__(kUnfThreads) void unfold_rows_e4m3_kernel(const RowItem* __restrict__ items,
                                                                        const uint8_t* __restrict__ folded,
                                                                        void* const* __restrict__ dsts,
@@ -64,36 +69,50 @@ __global__ __launch_bounds__(kUnfThreads) void unfold_rows_e4m3_kernel(const Row
   const int nq = 8 * it.nblk;        // 16-byte chunks of the run's folded row segments
   const int kc = (len + 30) / 16;    // chunks a row of len bytes can touch at any alignment
   const int total = it.rows * kc;
-  for (int c = t; c < total; c += kUnfThreads) {
-    const int r = c / kc, k = c - r * kc;
-    uint8_t* row = base + static_cast<int64_t>(r) * it.ld;
-    const int m = static_cast<int>(reinterpret_cast<uintptr_t>(row) & 15u);
-    const int x0 = 16 * k - m;  // run byte of the chunk's first byte (> -16)
-    if (x0 >= len) continue;
-    const uint8_t* srow = src + r * kB;
-    // run chunk q of row r: block q / 8 of the run, bytes 16 (q % 8) of its row segment
-    auto chunk = [&](int q) -> uint4 {
-      if (q < 0 || q >= nq) return make_uint4(0u, 0u, 0u, 0u);
-      return ld_stream(reinterpret_cast<const uint4*>(srow + static_cast<int64_t>(q >> 3) * kBlockElems +
-                                                      16 * (q & 7)));
-    };
-    const uint4 hi = chunk(k);
-    // chunk k - 1 of the row is the previous lane's chunk, unless this lane
-    // starts a wave or a row
-    uint4 prev;
-    prev.x = __shfl_up(hi.x, 1);
-    prev.y = __shfl_up(hi.y, 1);
-    prev.z = __shfl_up(hi.z, 1);
-    prev.w = __shfl_up(hi.w, 1);
-    const bool from_lane = (threadIdx.x & 63) != 0 && k > 0;
-    const uint4 x = m ? funnel16(from_lane ? prev : chunk(k - 1), hi, 16 - m) : hi;
-    uint8_t* d = row + x0;  // 16-byte aligned
-    if (x0 >= 0 && x0 + 16 <= len) {
-      st_global_stream(d, x);
-    } else {
-      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-      const int b0 = x0 < 0 ? -x0 : 0, b1 = len - x0 < 16 ? len - x0 : 16;
-      for (int b = b0; b < b1; ++b) d[b] = static_cast<uint8_t>(w[b >> 2] >> (8 * (b & 3)));
+  // kUnfBatch chunks per lane per round, every load of the round (the chunk, and
+  // chunk k - 1 where no lane has it) issued before any shuffle or store
+  constexpr int U = kUnfBatch;
+  for (int c0 = t; c0 < total; c0 += U * kUnfThreads) {
+    uint4 hi[U], lo[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kUnfThreads;
+      const int r = c / kc, k = c - r * kc;
+      const uint8_t* srow = src + r * kB;
+      const int m = static_cast<int>(reinterpret_cast<uintptr_t>(base + static_cast<int64_t>(r) * it.ld) & 15u);
+      const bool act = c < total && 16 * k - m < len;
+      // run chunk q of row r: block q / 8 of the run, bytes 16 (q % 8) of its row segment
+      hi[u] = act && k < nq ? ld_stream(reinterpret_cast<const uint4*>(srow + static_cast<int64_t>(k >> 3) * kBlockElems +
+                                                                    16 * (k & 7)))
+                            : make_uint4(0u, 0u, 0u, 0u);
+      const bool own_lo = m && act && k > 0 && (threadIdx.x & 63) == 0;  // no previous lane to take it from
+      lo[u] = own_lo ? ld_stream(reinterpret_cast<const uint4*>(srow + static_cast<int64_t>((k - 1) >> 3) * kBlockElems +
+                                                             16 * ((k - 1) & 7)))
+                     : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kUnfThreads;
+      uint4 prev;  // chunk k - 1 of the row is the previous lane's chunk (all lanes take part)
+      prev.x = __shfl_up(hi[u].x, 1);
+      prev.y = __shfl_up(hi[u].y, 1);
+      prev.z = __shfl_up(hi[u].z, 1);
+      prev.w = __shfl_up(hi[u].w, 1);
+      const int r = c / kc, k = c - r * kc;
+      uint8_t* row = base + static_cast<int64_t>(r) * it.ld;
+      const int m = static_cast<int>(reinterpret_cast<uintptr_t>(row) & 15u);
+      const int x0 = 16 * k - m;  // run byte of the chunk's first byte (> -16)
+      if (c >= total || x0 >= len) continue;
+      const bool from_lane = (threadIdx.x & 63) != 0 && k > 0;
+      const uint4 x = m ? funnel16(from_lane ? prev : lo[u], hi[u], 16 - m) : hi[u];
+      uint8_t* d = row + x0;  // 16-byte aligned
+      if (x0 >= 0 && x0 + 16 <= len) {
+        st_global_stream(d, x);
+      } else {
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        const int b0 = x0 < 0 ? -x0 : 0, b1 = len - x0 < 16 ? len - x0 : 16;
+        for (int b = b0; b < b1; ++b) d[b] = static_cast<uint8_t>(w[b >> 2] >> (8 * (b & 3)));
+      }
     }
   }
 }
