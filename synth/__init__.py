@@ -197,6 +197,13 @@ SMALL_WORKLOADS = {
     "wide_rows_small": Workload(
         name="wide_rows_small", shapes=((1, 150, 40000), (1, 300, 520)), dp=2, ranks=(0, 1), steps=2,
         hp=TINY_HP, grad_sigma=1e-3),
+    # columns in whole 128-column blocks (every row-major block row segment starts
+    # on a 128-byte line of an aligned array), ragged row counts; the full_small
+    # recipe otherwise, on two ranks
+    "lines_small": Workload(
+        name="lines_small", shapes=((4, 300, 512), (1, 200, 256)), dp=2, ranks=(0, 1), steps=5,
+        hp=dataclasses.replace(TINY_HP, max_grad_norm=1.0, loss_scaling=True, init_scale=65536.0),
+        master_dtype="bf16", grad_sigma=1e-4, grad_premult=65536.0, inf_block=(3, 0, 1, 2, 3)),
     "full_small": Workload(
         name="full_small", shapes=((4, 300, 520),), dp=1, ranks=(0,), steps=5,
         hp=dataclasses.replace(TINY_HP, max_grad_norm=1.0, loss_scaling=True, init_scale=65536.0),

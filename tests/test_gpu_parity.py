@@ -303,7 +303,7 @@ def _run_parity(w, ranks=None, fused=None, fold_on_read=False):
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_clip", "tiny_lossscale", "dense_small", "moe_small", "full_small",
-                                  "tiny_pow2", "ragged_small_pow2"])
+                                  "lines_small", "tiny_pow2", "ragged_small_pow2"])
 @pytest.mark.parametrize("fold_on_read", [False, True])
 def test_step_parity(name, fold_on_read):
     _run_parity(synth.get(name), fold_on_read=fold_on_read)
