@@ -25,10 +25,12 @@ class Shard:
         self.n_slots = n
         dev = torch.device(device)
         f32 = dict(dtype=torch.float32, device=dev)
-        self.grad = torch.zeros(n * BLOCK_ELEMS, **f32)
-        self.master = torch.zeros(n * BLOCK_ELEMS, **f32)
-        self.m = torch.zeros(n * BLOCK_ELEMS, **f32)
-        self.v = torch.zeros(n * BLOCK_ELEMS, **f32)
+        # the four float32 shard buffers back to back in one allocation: on
+        # MI355X the update of the MoE expert shard ran 2 % faster so than with
+        # four separate allocations, whose relative placement is left to the
+        # allocator
+        self._fp32 = torch.zeros(4 * n * BLOCK_ELEMS, **f32)
+        self.grad, self.master, self.m, self.v = self._fp32.view(4, n * BLOCK_ELEMS).unbind(0)
         self.fp8 = torch.zeros(n * BLOCK_ELEMS, dtype=torch.uint8, device=dev)
         self.scales = torch.zeros(max(n, 1), **f32)
         self.workspace = torch.zeros(max(n * L.STAT_PARTS, 1), dtype=torch.float64, device=dev)
