@@ -461,6 +461,39 @@ def test_dequantize_every_code(shape):
     assert gb[~nan].tobytes() == wb[~nan].tobytes()
 
 
+@pytest.mark.parametrize("shape", [(1, 256, 2048), (1, 130, 300)])
+def test_dequantize_extreme_scales(shape):
+    """Every code times block scales at the ends of the float32 range: products that
+    are subnormal or round to zero, scales that are subnormal themselves, products
+    that overflow to infinity (and, in BF16, finite floats that round up to it).
+    Float32 bit-exact against the oracle, bfloat16 equal to torch's RNE cast of it;
+    C = 2048 takes the vector kernel, C = 300 the any-alignment one."""
+    from oracle import quant as oquant
+    codes = (np.arange(int(np.prod(shape))) % 256).astype(np.uint8).reshape(shape)
+    picks = np.array([2.0 ** -149, 2.0 ** -140, 2.0 ** -130, 2.0 ** -127, 2.0 ** -126, 1.1754942e-38 * 0.75,
+                      1e-30, 2.0 ** -9, 1.0 / 448, 1.0, 3.0, 2.0 ** 100, 2.0 ** 119, 1e36, 3.0e38,
+                      float(np.finfo(np.float32).max)], dtype=np.float64).astype(np.float32)
+    g = otable.grid(shape)
+    scales = picks[(5 * np.arange(int(np.prod(g)))) % len(picks)].reshape(g)  # both ends in any grid
+    want = oquant.dequantize(codes, scales)
+    assert np.isinf(want).any() and (want[np.isfinite(want)] != 0).any()
+    tiny = np.abs(want[np.isfinite(want)])
+    assert ((tiny > 0) & (tiny < np.finfo(np.float32).tiny)).any(), "some products must be subnormal"
+    dc, ds = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
+    out = torch.empty(shape, dtype=torch.float32, device="cuda")
+    fz.fp8z1_dequantize(dc, ds, shape, fz.F32, out)
+    got = out.cpu().numpy()
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all()
+    assert got[~nan].tobytes() == want[~nan].tobytes()
+    ob = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    fz.fp8z1_dequantize(dc, ds, shape, fz.BF16, ob)
+    gb = ob.float().cpu().numpy()
+    wb = torch.from_numpy(want).to(torch.bfloat16).float().numpy()
+    assert (np.isnan(gb) == nan).all()
+    assert gb[~nan].tobytes() == wb[~nan].tobytes()
+
+
 @pytest.mark.parametrize("name", ["moe_small", "full_small"])
 def test_dequantized_weights_track_the_master(name):
     """After a few steps the dequantized FP8 weights stay close to the FP32 master:
