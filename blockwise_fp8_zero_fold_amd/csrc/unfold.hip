@@ -118,13 +118,16 @@ __global__ __launch_bounds__(kUnfThreads) void unfold_rows_e4m3_kernel(const Row
 }
 
 // FP8 codes, by blocks (used when every row segment of the call starts on a
-// 128-byte line, so no line is shared by two workgroups): a workgroup moves
-// a quarter of a block (32 rows x 128 bytes, 4 KB), so that the workgroups in
-// flight cover a compact range of memory; 8 lanes per row, 16 bytes each.
-constexpr int kUnfRows = 32;
+// 128-byte line, so no line is shared by two workgroups): a workgroup of one
+// wave moves a sixteenth of a block (8 rows x 128 bytes, 1 KB), so that the
+// workgroups in flight cover a compact range of memory; 8 lanes per row, 16
+// bytes each.  (4 KB per workgroup of 256 lanes took 2-3 % longer, 8 and
+// 16 KB with two or four rows per lane 12-17 %.)
+constexpr int kUnfRows = 8;
 constexpr int kUnfParts = kB / kUnfRows;
+constexpr int kUnfBlkThreads = 8 * kUnfRows;
 
-__global__ __launch_bounds__(kUnfThreads) void unfold_blocks_e4m3_kernel(const SlotPlan* __restrict__ plan,
+__global__ __launch_bounds__(kUnfBlkThreads) void unfold_blocks_e4m3_kernel(const SlotPlan* __restrict__ plan,
                                                                          const uint8_t* __restrict__ folded,
                                                                          void* const* __restrict__ dsts,
                                                                          const float* __restrict__ scales,
@@ -235,7 +238,7 @@ extern "C" int fp8z1_unfold(const fp8z1_table* ct, const void* folded, int32_t d
     for (size_t p = 0; p < t->shapes.size() && lines; ++p)
       if (t->held[p]) lines = t->shapes[p].C % 128 == 0 && reinterpret_cast<uintptr_t>(dst[p]) % 128 == 0;
     if (lines)
-      hipLaunchKernelGGL(unfold_blocks_e4m3_kernel, dim3(static_cast<unsigned>(n * kUnfParts)), dim3(kUnfThreads), 0, s,
+      hipLaunchKernelGGL(unfold_blocks_e4m3_kernel, dim3(static_cast<unsigned>(n * kUnfParts)), dim3(kUnfBlkThreads), 0, s,
                          t->d_plan,
                          static_cast<const uint8_t*>(folded), ddst, with_scales ? scales : nullptr,
                          reinterpret_cast<float* const*>(dsc));
