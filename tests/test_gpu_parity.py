@@ -581,6 +581,28 @@ def test_random_shape_sets(seed):
     _run_parity(w, fold_on_read=True)
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_hyperparameters(seed):
+    """AdamW and loss-scale settings away from the usual ones: learning rates from
+    1e-5 to 0.3, beta1 and beta2 down to 0 and up to 0.9999, eps from 1e-12 to 1e-3,
+    weight decay from 0 to 1, growth and backoff factors other than 2 and 0.5, over
+    five steps on both routes and every rank, bit for bit against the oracle."""
+    rng = np.random.default_rng(2000 + seed)
+    pick = lambda xs: float(rng.choice(xs))
+    hp = synth.Hparams(lr=float(10.0 ** rng.uniform(-5, np.log10(0.3))), beta1=pick([0.0, 0.5, 0.9, 0.99]),
+                       beta2=pick([0.0, 0.9, 0.999, 0.9999]), eps=pick([1e-12, 1e-8, 1e-3]),
+                       weight_decay=pick([0.0, 0.01, 0.1, 1.0]), max_grad_norm=pick([0.0, 0.01, 1.0]),
+                       loss_scaling=bool(rng.integers(0, 2)), init_scale=pick([1.0, 256.0, 2.0 ** 20]),
+                       growth_factor=pick([1.5, 2.0, 4.0]), backoff_factor=pick([0.25, 0.5, 0.75]),
+                       growth_interval=int(rng.integers(1, 4)), scale_rule=int(rng.integers(0, 2)))
+    w = synth.Workload(name=f"hparams{seed}", shapes=((2, 200, 300), (1, 256, 128)), dp=2, ranks=(0, 1), steps=5,
+                       hp=hp, grad_sigma=1e-3, grad_premult=hp.init_scale if hp.loss_scaling else 1.0,
+                       inf_block=(3, 0, 1, 1, 2) if seed % 2 else None)
+    print(f"# {w.name}: {hp}", flush=True)
+    _run_parity(w)
+    _run_parity(w, fold_on_read=True)
+
+
 @pytest.mark.parametrize("name,rank,mode", [("tiny_clip", 1, "eager"), ("full_small", 0, "graph")])
 def test_c_abi_consumer_without_python(tmp_path, name, rank, mode):
     """A C++ program (tests/native/abi_c_step.cpp, built with the library) drives the
