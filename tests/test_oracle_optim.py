@@ -58,6 +58,27 @@ def test_adamw_matches_float64_brute_force():
     assert np.all(np.abs(v - ref[:, 2]) <= 1e-6 * np.abs(ref[:, 2]))
 
 
+@pytest.mark.parametrize("kw", [dict(beta1=0.0, beta2=0.0), dict(beta1=0.99, beta2=0.9999),
+                                dict(lr=0.3, weight_decay=1.0), dict(eps=1e-3, weight_decay=0.0),
+                                dict(lr=1e-5, eps=1e-12, beta1=0.5, beta2=0.9)])
+def test_adamw_brute_force_unusual_hyperparameters(kw):
+    """The same float64 brute force with betas at 0 and near 1, a large learning rate with
+    full weight decay, a large eps, a tiny learning rate and eps."""
+    import dataclasses
+    hp = dataclasses.replace(HP, **kw)
+    rng = np.random.default_rng(1)
+    n = 2000
+    p0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g = (rng.standard_normal((n, 3)) * rng.choice([1e-6, 1e-3, 1.0], (n, 1))).astype(np.float32)
+    p, m, v, ks = _run_oracle(g, p0, hp)
+    ref = _brute_adamw_f64(g, p0, hp, [1.0, 1.0, 1.0])
+    lr = float(np.float32(hp.lr))
+    assert np.all(np.abs(p - ref[:, 0]) <= 1e-6 * np.abs(ref[:, 0]) + 1e-6 * lr), kw
+    gmax = np.max(np.abs(g.astype(np.float64)), axis=1)
+    assert np.all(np.abs(m - ref[:, 1]) <= 1e-6 * gmax), kw
+    assert np.all(np.abs(v - ref[:, 2]) <= 1e-6 * np.abs(ref[:, 2]) + 1e-30), kw
+
+
 def test_adamw_with_clipping_matches_brute_force():
     rng = np.random.default_rng(1)
     n = 3000
